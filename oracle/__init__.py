@@ -1,0 +1,243 @@
+"""CPU oracle for the ConvRot int8 quantized linear (test infrastructure).
+
+Only the tests, the smoke check and the benchmark's CPU-baseline leg may import
+this package.  The product library never loads it and shares no code with it.
+
+The arithmetic lives in ``convrot_oracle.c`` (plain scalar C, built with gcc
+``-O2 -ffp-contract=off -fno-fast-math``); this module builds it on first use,
+loads it with ctypes and wraps each function for numpy arrays.  Every wrapper
+states the step it computes; the C file cites the passages of the pages each
+step follows.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "convrot_oracle.c")
+_LIB = os.path.join(_HERE, "libconvrot_oracle.so")
+
+GROUP = 256
+
+_CFLAGS = ["-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp",
+           "-ffp-contract=off", "-fno-fast-math", "-Wall", "-Wextra"]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc into ``oracle/libconvrot_oracle.so``."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.run(["gcc", *_CFLAGS, _SRC, "-o", tmp, "-lm"], check=True)
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        build()
+        L = ctypes.CDLL(_LIB)
+        P = ctypes.c_void_p
+        I64 = ctypes.c_int64
+        L.orc_set_threads.argtypes = [ctypes.c_int]
+        L.orc_get_threads.restype = ctypes.c_int
+        L.orc_bf16_to_f32_one.argtypes = [ctypes.c_uint16]
+        L.orc_bf16_to_f32_one.restype = ctypes.c_float
+        L.orc_f32_to_bf16_one.argtypes = [ctypes.c_float]
+        L.orc_f32_to_bf16_one.restype = ctypes.c_uint16
+        L.orc_bf16_to_f32.argtypes = [P, P, I64]
+        L.orc_f32_to_bf16.argtypes = [P, P, I64]
+        L.orc_fwht256.argtypes = [P]
+        L.orc_rotate_rows.argtypes = [P, I64, I64]
+        L.orc_quantize_row.argtypes = [P, I64, P, P]
+        L.orc_quantize_rows.argtypes = [P, I64, I64, P, P]
+        L.orc_quantize_weight.argtypes = [P, I64, I64, P, P]
+        L.orc_quantize_weight.restype = ctypes.c_int
+        L.orc_rotate_quant_act_rows.argtypes = [P, I64, P, I64, P, P]
+        L.orc_rotate_quant_act_rows.restype = ctypes.c_int
+        L.orc_gemm_s32.argtypes = [P, I64, P, I64, I64, P]
+        L.orc_dequant_one.argtypes = [ctypes.c_int32, ctypes.c_float, ctypes.c_float]
+        L.orc_dequant_one.restype = ctypes.c_float
+        L.orc_dequant_bf16.argtypes = [P, I64, I64, P, P, P]
+        L.orc_exp.argtypes = [ctypes.c_float]
+        L.orc_exp.restype = ctypes.c_float
+        L.orc_silu.argtypes = [ctypes.c_float]
+        L.orc_silu.restype = ctypes.c_float
+        L.orc_swiglu_bf16.argtypes = [P, I64, I64, P, P, P]
+        _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray) -> int:
+    assert a.flags.c_contiguous
+    return a.ctypes.data
+
+
+def set_threads(n: int) -> None:
+    lib().orc_set_threads(int(n))
+
+
+def get_threads() -> int:
+    return int(lib().orc_get_threads())
+
+
+# ------------------------------------------------------------------ formats
+
+def bf16_to_f32(h: np.ndarray) -> np.ndarray:
+    """Exact widening of raw bf16 bits (uint16) to fp32."""
+    h = np.ascontiguousarray(h, dtype=np.uint16)
+    out = np.empty(h.shape, np.float32)
+    lib().orc_bf16_to_f32(_p(h), _p(out), h.size)
+    return out
+
+
+def f32_to_bf16(f: np.ndarray) -> np.ndarray:
+    """fp32 -> raw bf16 bits, round to nearest even."""
+    f = np.ascontiguousarray(f, dtype=np.float32)
+    out = np.empty(f.shape, np.uint16)
+    lib().orc_f32_to_bf16(_p(f), _p(out), f.size)
+    return out
+
+
+# ------------------------------------------------------------------ rotation
+
+def fwht256(v: np.ndarray) -> np.ndarray:
+    """Normalized 256-point Walsh-Hadamard transform of one fp32 vector."""
+    v = np.array(v, dtype=np.float32, copy=True).reshape(GROUP)
+    lib().orc_fwht256(_p(v))
+    return v
+
+
+def rotate_rows(x: np.ndarray) -> np.ndarray:
+    """Group-wise rotation of every row of an fp32 [rows, k] array."""
+    x = np.array(x, dtype=np.float32, copy=True, order="C")
+    rows, k = x.shape
+    assert k % GROUP == 0
+    lib().orc_rotate_rows(_p(x), rows, k)
+    return x
+
+
+# ------------------------------------------------------------------ quantizer
+
+def quantize_rows(v: np.ndarray):
+    """Per-row symmetric int8 of fp32 rows as given (no rotation)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    rows, k = v.shape
+    q = np.empty((rows, k), np.int8)
+    s = np.empty(rows, np.float32)
+    lib().orc_quantize_rows(_p(v), rows, k, _p(q), _p(s))
+    return q, s
+
+
+def quantize_weight(w: np.ndarray):
+    """Rotate each row of fp32 W [n, k] along k and quantize it per row."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    n, k = w.shape
+    q = np.empty((n, k), np.int8)
+    s = np.empty(n, np.float32)
+    rc = lib().orc_quantize_weight(_p(w), n, k, _p(q), _p(s))
+    if rc != 0:
+        raise ValueError("oracle quantize_weight failed (k=%d)" % k)
+    return q, s
+
+
+def rotate_quant_act(x_bf16: np.ndarray, rows: np.ndarray | None = None):
+    """Widen bf16 x [m, k], rotate along k, quantize per token.
+
+    With ``rows`` given, only those rows are processed (in that order)."""
+    x_bf16 = np.ascontiguousarray(x_bf16, dtype=np.uint16)
+    m, k = x_bf16.shape
+    if rows is None:
+        nrows, rp = m, None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        assert rows.size == 0 or (rows.min() >= 0 and rows.max() < m)
+        nrows, rp = rows.size, _p(rows)
+    q = np.empty((nrows, k), np.int8)
+    s = np.empty(nrows, np.float32)
+    rc = lib().orc_rotate_quant_act_rows(_p(x_bf16), k, rp, nrows, _p(q), _p(s))
+    if rc != 0:
+        raise ValueError("oracle rotate_quant_act failed (k=%d)" % k)
+    return q, s
+
+
+# ------------------------------------------------------------------ contraction
+
+def gemm_s32(qx: np.ndarray, qw: np.ndarray) -> np.ndarray:
+    """int32 acc[j, c] = sum_k qx[j, k] * qw[c, k] (triple loop)."""
+    qx = np.ascontiguousarray(qx, dtype=np.int8)
+    qw = np.ascontiguousarray(qw, dtype=np.int8)
+    nrows, k = qx.shape
+    n, k2 = qw.shape
+    assert k == k2
+    acc = np.empty((nrows, n), np.int32)
+    lib().orc_gemm_s32(_p(qx), nrows, _p(qw), n, k, _p(acc))
+    return acc
+
+
+# ------------------------------------------------------------------ epilogues
+
+def dequant_bf16(acc: np.ndarray, s_x: np.ndarray, s_w: np.ndarray) -> np.ndarray:
+    """bf16(((float)acc * s_x[row]) * s_w[col])."""
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    s_x = np.ascontiguousarray(s_x, dtype=np.float32)
+    s_w = np.ascontiguousarray(s_w, dtype=np.float32)
+    nrows, n = acc.shape
+    assert s_x.size == nrows and s_w.size == n
+    y = np.empty((nrows, n), np.uint16)
+    lib().orc_dequant_bf16(_p(acc), nrows, n, _p(s_x), _p(s_w), _p(y))
+    return y
+
+
+def dequant_f32(acc: np.ndarray, s_x: np.ndarray, s_w: np.ndarray) -> np.ndarray:
+    """The fp32 value before bf16 rounding, element by element (small inputs)."""
+    L = lib()
+    out = np.empty(acc.shape, np.float32)
+    for j in range(acc.shape[0]):
+        for c in range(acc.shape[1]):
+            out[j, c] = L.orc_dequant_one(int(acc[j, c]), float(s_x[j]), float(s_w[c]))
+    return out
+
+
+def exp(x: float) -> float:
+    return float(lib().orc_exp(float(x)))
+
+
+def silu(g: float) -> float:
+    return float(lib().orc_silu(float(g)))
+
+
+def swiglu_bf16(acc: np.ndarray, s_x: np.ndarray, s_w: np.ndarray) -> np.ndarray:
+    """bf16(silu(g) * u), g from columns [0, i), u from columns [i, 2i)."""
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    s_x = np.ascontiguousarray(s_x, dtype=np.float32)
+    s_w = np.ascontiguousarray(s_w, dtype=np.float32)
+    nrows, n2 = acc.shape
+    assert n2 % 2 == 0 and s_w.size == n2 and s_x.size == nrows
+    i = n2 // 2
+    y = np.empty((nrows, i), np.uint16)
+    lib().orc_swiglu_bf16(_p(acc), nrows, i, _p(s_x), _p(s_w), _p(y))
+    return y
+
+
+# ------------------------------------------------------------------ compositions
+
+def linear_rows(x_bf16, q_w, s_w, rows=None):
+    """y rows of the ConvRot linear: rotate+quantize x, int32 GEMM, dequant."""
+    qx, sx = rotate_quant_act(x_bf16, rows)
+    acc = gemm_s32(qx, q_w)
+    return dequant_bf16(acc, sx, s_w)
+
+
+def linear_swiglu_rows(x_bf16, q_w, s_w, rows=None):
+    """y rows of the ConvRot fc1 with fused SwiGLU (q_w holds 2i rows)."""
+    qx, sx = rotate_quant_act(x_bf16, rows)
+    acc = gemm_s32(qx, q_w)
+    return swiglu_bf16(acc, sx, s_w)

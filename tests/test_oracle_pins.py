@@ -1,0 +1,542 @@
+"""Pins of the CPU oracle against what the definitions fix (CPU only).
+
+Every check compares the oracle with something other than itself: the closed
+form of the Sylvester Hadamard matrix, exact integer arithmetic, fp64 dense
+linear algebra with a stated rounding bound, numpy's int64 matmul, torch's
+bf16 cast, Python's correctly rounded fp64 exp, or a value fixed by the
+mathematics of a constructed input.  A plausible slip in the oracle (a wrong
+stage order or sign, a dropped 1/16, a transposed operand, round-half-up
+instead of half-even, a swapped gate/up half, scales applied to the wrong
+axis) fails at least one of them.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+from tests import hadamard as hd
+import workloads
+
+U = 2.0 ** -24
+GAMMA8 = 8 * U / (1 - 8 * U)
+
+
+# ------------------------------------------------------------------ Hadamard
+
+def test_sylvester_definition():
+    """H.H = 256 I and H = H^T for the closed-form Sylvester matrix (C1)."""
+    H = hd.H()
+    assert np.array_equal(H, H.T)
+    assert np.array_equal(H @ H, 256 * np.eye(256, dtype=np.int64))
+    # Sylvester recursion H_2n = [[H, H], [H, -H]] holds on every level
+    for n in (2, 4, 8, 16, 32, 64, 128):
+        a = hd.sylvester(n)
+        b = hd.sylvester(2 * n)
+        assert np.array_equal(b, np.block([[a, a], [a, -a]]))
+
+
+def test_fwht_basis_columns():
+    """fwht(e_j) is column j of H/16, exactly, for every j (C2)."""
+    H = hd.H()
+    for j in range(256):
+        e = np.zeros(256, np.float32)
+        e[j] = 1.0
+        got = oracle.fwht256(e)
+        assert np.array_equal(got.astype(np.float64), H[:, j] / 16.0), j
+
+
+def test_fwht_exact_integer_regime():
+    """For integers |x| <= 2^15 every partial sum is an integer below 2^24, so the
+    fp32 butterfly must equal the dense integer product H.x / 16 bit for bit (C3)."""
+    rng = np.random.default_rng(11)
+    H = hd.H()
+    for _ in range(200):
+        x = rng.integers(-2 ** 15, 2 ** 15 + 1, 256)
+        got = oracle.fwht256(x.astype(np.float32)).astype(np.float64)
+        want = (H @ x).astype(np.float64) / 16.0
+        assert np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("kind", ["normal", "outliers", "laplace", "wide"])
+def test_fwht_rounding_bound(kind):
+    """Depth-8 pairwise summation bound: |fwht(x)_i - (H x / 16)_i| <=
+    gamma_8 * sum_j |x_j| / 16, with the reference in fp64 (C4)."""
+    rng = np.random.default_rng(12)
+    H = hd.H().astype(np.float64)
+    for _ in range(100):
+        if kind == "normal":
+            x = rng.standard_normal(256).astype(np.float32)
+        elif kind == "outliers":
+            x = rng.standard_normal(256).astype(np.float32)
+            x[rng.choice(256, 3, replace=False)] *= 50
+        elif kind == "laplace":
+            x = rng.laplace(size=256).astype(np.float32)
+        else:
+            x = (rng.standard_normal(256) * np.exp2(rng.integers(-20, 20, 256))).astype(np.float32)
+        got = oracle.fwht256(x).astype(np.float64)
+        want = H @ x.astype(np.float64) / 16.0
+        bound = GAMMA8 * np.abs(x.astype(np.float64)).sum() / 16.0
+        assert np.all(np.abs(got - want) <= bound)
+
+
+def test_norm_preservation_and_involution():
+    """H/16 is orthogonal and involutive: ||fwht(x)|| = ||x|| and
+    fwht(fwht(x)) = x, up to the fp32 rounding of 8 stages (C5)."""
+    rng = np.random.default_rng(13)
+    for _ in range(100):
+        x = rng.standard_normal(256).astype(np.float32)
+        y = oracle.fwht256(x)
+        nx = np.linalg.norm(x.astype(np.float64))
+        assert abs(np.linalg.norm(y.astype(np.float64)) - nx) <= 16 * GAMMA8 * nx
+        z = oracle.fwht256(y).astype(np.float64)
+        bound = 2 * GAMMA8 * np.abs(x.astype(np.float64)).sum() / 16.0 * 16
+        assert np.max(np.abs(z - x)) <= bound
+    # the exact regime: a second pass returns integer inputs exactly
+    x = np.random.default_rng(14).integers(-2000, 2000, 256).astype(np.float32)
+    assert np.array_equal(oracle.fwht256(oracle.fwht256(x)), x)
+
+
+def test_rotation_is_groupwise_and_contiguous():
+    """Each contiguous 256-block of a row is rotated on its own: perturbing one
+    block changes only that block's outputs (reading: groups of the conv with
+    kernel = stride = 256)."""
+    rng = np.random.default_rng(15)
+    x = rng.standard_normal((3, 1024)).astype(np.float32)
+    r = oracle.rotate_rows(x)
+    x2 = x.copy()
+    x2[1, 300] += 1.0
+    r2 = oracle.rotate_rows(x2)
+    diff = np.nonzero(np.any(r != r2, axis=0))[0]
+    assert diff.min() >= 256 and diff.max() < 512
+    assert np.array_equal(r[0], r2[0]) and np.array_equal(r[2], r2[2])
+    # and matches the dense fp64 block-diagonal rotation within the bound
+    want = hd.rotate_fp64(x)
+    for g in range(4):
+        bound = GAMMA8 * np.abs(x[:, g * 256:(g + 1) * 256].astype(np.float64)).sum(1) / 16
+        assert np.all(np.abs(r[:, g * 256:(g + 1) * 256] - want[:, g * 256:(g + 1) * 256])
+                      <= bound[:, None])
+
+
+def test_rotation_invariance_of_the_product():
+    """(x H)(W H)^T = x W^T: the oracle's fp32 rotation of both operands keeps the
+    fp64 product within the propagated butterfly bound, on all of config 1 (C6)."""
+    d = workloads.make_linear(1)
+    x = hd.bf16_bits_to_f64(d["x"])
+    w = d["w"].astype(np.float64)
+    xr = oracle.rotate_rows(x.astype(np.float32)).astype(np.float64)
+    wr = oracle.rotate_rows(d["w"]).astype(np.float64)
+    exact = x @ w.T
+    got = xr @ wr.T
+
+    def err(a):
+        e = np.empty_like(a)
+        for g in range(0, a.shape[1], 256):
+            e[:, g:g + 256] = GAMMA8 * np.abs(a[:, g:g + 256]).sum(1, keepdims=True) / 16
+        return e
+    ex, ew = err(x), err(w)
+    bound = ex @ np.abs(wr).T + np.abs(xr) @ ew.T + ex @ ew.T
+    bound = bound * (1 + 1e-6) + 1e-12 * (np.abs(x) @ np.abs(w).T)
+    assert np.all(np.abs(got - exact) <= bound)
+
+
+# ------------------------------------------------------------------ quantizer
+
+def _check_quant_invariants(v, q, s):
+    v64 = v.astype(np.float64)
+    assert q.dtype == np.int8
+    assert q.min() >= -127 and q.max() <= 127
+    for r in range(v.shape[0]):
+        amax = np.abs(v64[r]).max()
+        if amax == 0:
+            assert s[r] == 0 and not q[r].any()
+            continue
+        # s is amax / 127 correctly rounded (within half an ulp of the exact quotient)
+        assert abs(float(s[r]) - amax / 127) <= 0.5 * float(np.spacing(np.float32(s[r])))
+        am = np.argmax(np.abs(v64[r]))
+        assert abs(int(q[r, am])) == 127 and np.sign(q[r, am]) == np.sign(v64[r, am])
+        # round-trip bound |v - q s| <= s/2 + |v| 2^-24 (division rounding), fp64 slack
+        s64 = float(s[r])
+        lhs = np.abs(v64[r] - q[r].astype(np.float64) * s64)
+        assert np.all(lhs <= s64 / 2 + np.abs(v64[r]) * 2.0 ** -24 + 1e-12 * s64)
+
+
+def test_quantizer_invariants():
+    """Codes in [-127, 127], |q| = 127 at the row's argmax, the round-trip
+    bound, and an all-zero row giving s = 0 and zero codes (C7, S9)."""
+    rng = np.random.default_rng(16)
+    v = rng.standard_normal((40, 512)).astype(np.float32)
+    v[3] = 0.0
+    v[5] *= 1e-30
+    v[7, 17] = 1e6
+    v[9] = np.float32(2.0) ** rng.integers(-60, 60, 512)
+    q, s = oracle.quantize_rows(v)
+    _check_quant_invariants(v, q, s)
+    d = workloads.make_linear(1)
+    qx, sx = oracle.rotate_quant_act(d["x"])
+    xr = oracle.rotate_rows(oracle.bf16_to_f32(d["x"]))
+    _check_quant_invariants(xr, qx, sx)
+    qw, sw = oracle.quantize_weight(d["w"])
+    _check_quant_invariants(oracle.rotate_rows(d["w"]), qw, sw)
+
+
+def _tie_row(k, scale, rng, values):
+    """A bf16-exact activation row whose rotation is sparse: group g holds
+    v_g * (column j_g of H/16), so the rotated row is v_g at position j_g.
+    Returns x (fp64), the rotated row (exact), and the expected codes."""
+    H = hd.H().astype(np.float64)
+    x = np.zeros(k)
+    rot = np.zeros(k)
+    for g, val in enumerate(values):
+        j = int(rng.integers(0, 256))
+        x[g * 256:(g + 1) * 256] = val * scale * H[:, j] / 16.0
+        rot[g * 256 + j] = val * scale
+    return x, rot
+
+
+def test_tie_breaking_half_even_activation_path():
+    """Rotated values that are exact half-integers of the scale must round half
+    to even: 2.5 -> 2, 3.5 -> 4, -2.5 -> -2, -0.5 -> 0, 126.5 -> 126 (C8, S8).
+    The amax entry is 127 * 2^e so s = 2^e exactly; all inputs are bf16-exact."""
+    rng = np.random.default_rng(17)
+    values = [127.0, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5, -1.5, 126.5, -126.5, 4.5, -3.5, 0.0, 5.5, 6.5, -7.5]
+    k = 256 * len(values)
+    rows, expect, scales = [], [], []
+    for e in (0, -3, 5, -10):
+        x, rot = _tie_row(k, 2.0 ** e, rng, values)
+        assert hd.is_bf16_exact(x)
+        rows.append(x)
+        expect.append(np.rint(rot / 2.0 ** e))  # numpy rint: exact halves to even
+        scales.append(2.0 ** e)
+    xb = workloads.to_bf16_bits(np.array(rows, np.float32))
+    q, s = oracle.rotate_quant_act(xb)
+    assert np.array_equal(s.astype(np.float64), np.array(scales))
+    assert np.array_equal(q.astype(np.float64), np.array(expect))
+    want = {2.5: 2, 3.5: 4, -2.5: -2, -0.5: 0, 126.5: 126, 0.5: 0, 1.5: 2, -1.5: -2, 4.5: 4}
+    for v, c in want.items():
+        assert int(np.rint(v)) == c
+
+
+def test_tie_breaking_weight_path_dense():
+    """Weight path (fp32 input): W = H v / 16 with dense half-integer v and
+    amax 127 is exact in fp32, its rotation returns v exactly, and the codes are
+    v rounded half to even (C8)."""
+    rng = np.random.default_rng(18)
+    H = hd.H()
+    v = rng.integers(-254, 255, (6, 512)).astype(np.float64) / 2.0  # halves in [-127, 127]
+    v[:, 5] = 127.0
+    w = np.zeros_like(v)
+    for g in range(2):
+        w[:, g * 256:(g + 1) * 256] = v[:, g * 256:(g + 1) * 256] @ H / 16.0
+    assert np.array_equal(w.astype(np.float32).astype(np.float64), w)
+    q, s = oracle.quantize_weight(w.astype(np.float32))
+    assert np.all(s == 1.0)
+    assert np.array_equal(q.astype(np.float64), np.rint(v))
+    assert np.any(np.abs(v - np.trunc(v)) == 0.5)
+
+
+def test_dense_bruteforce_tiny():
+    """Rotate and quantize in fp64 from the dense matrix; the oracle's codes must
+    equal it except where v/s sits within 1e-5 of a half-integer, and the
+    oracle's scales agree to fp32 rounding (C11)."""
+    rng = np.random.default_rng(19)
+    for trial in range(6):
+        m, k = 16, 256 * (1 + trial % 3)
+        x = rng.standard_normal((m, k)).astype(np.float32)
+        x[:, rng.choice(k, 2, replace=False)] *= 40
+        xb = workloads.to_bf16_bits(x)
+        q, s = oracle.rotate_quant_act(xb)
+        v = hd.rotate_fp64(hd.bf16_bits_to_f64(xb))
+        s64 = np.abs(v).max(1) / 127
+        assert np.all(np.abs(s - s64) <= 2 * U * s64)
+        t = v / s64[:, None]
+        q64 = np.clip(np.rint(t), -127, 127)
+        mism = q.astype(np.float64) != q64
+        near = np.abs(np.abs(t - np.trunc(t)) - 0.5) < 1e-5
+        assert np.all(near[mism]), (trial, np.argwhere(mism & ~near)[:5])
+
+
+# ------------------------------------------------------------------ contraction
+
+def test_gemm_s32_matches_int64_matmul():
+    """The int32 triple loop equals numpy's int64 matmul on random codes (C9)."""
+    rng = np.random.default_rng(20)
+    for (m, n, k) in [(1, 1, 256), (7, 13, 512), (33, 17, 1024), (64, 256, 512)]:
+        a = rng.integers(-127, 128, (m, k)).astype(np.int8)
+        b = rng.integers(-127, 128, (n, k)).astype(np.int8)
+        want = a.astype(np.int64) @ b.astype(np.int64).T
+        got = oracle.gemm_s32(a, b)
+        assert got.dtype == np.int32 and np.array_equal(got.astype(np.int64), want)
+    # not symmetric in its operands: a transposed operand would fail here
+    a = rng.integers(-127, 128, (3, 256)).astype(np.int8)
+    b = rng.integers(-127, 128, (5, 256)).astype(np.int8)
+    assert oracle.gemm_s32(a, b).shape == (3, 5)
+
+
+def test_gemm_closed_form_extremes():
+    """All codes +127 at K = 14336 give 127^2 * 14336 = 231,225,344 exactly, and
+    mixed signs give the negative (C9); 127^2 * 133120 still fits int32."""
+    k = 14336
+    a = np.full((2, k), 127, np.int8)
+    b = np.full((3, k), 127, np.int8)
+    b[1] = -127
+    got = oracle.gemm_s32(a, b)
+    assert got[0, 0] == 231225344 and got[1, 1] == -231225344
+    assert 127 * 127 * 133120 < 2 ** 31 <= 127 * 127 * 133376
+
+
+def test_closed_form_single_code():
+    """x = c * (column j of H/16) in one group, W = d * (column j of H/16): both
+    quantize to a single code of +-127 at j, acc = +-16129, and the output is the
+    exact product c * d up to the fp32 scales and bf16 rounding (C10)."""
+    H = hd.H().astype(np.float64)
+    for (c, d, j, g) in [(3.0, 0.5, 7, 0), (-2.0, 0.25, 200, 1), (48.0, -0.0625, 0, 1), (1.5, 1.5, 255, 0)]:
+        x = np.zeros((1, 512))
+        w = np.zeros((1, 512))
+        x[0, g * 256:(g + 1) * 256] = c * H[:, j] / 16
+        w[0, g * 256:(g + 1) * 256] = d * H[:, j] / 16
+        assert hd.is_bf16_exact(x)
+        xb = workloads.to_bf16_bits(x.astype(np.float32))
+        qx, sx = oracle.rotate_quant_act(xb)
+        qw, sw = oracle.quantize_weight(w.astype(np.float32))
+        assert np.count_nonzero(qx) == 1 and qx[0, g * 256 + j] == 127 * np.sign(c)
+        assert np.count_nonzero(qw) == 1 and qw[0, g * 256 + j] == 127 * np.sign(d)
+        acc = oracle.gemm_s32(qx, qw)
+        assert acc[0, 0] == 16129 * np.sign(c * d)
+        y = hd.bf16_bits_to_f64(oracle.dequant_bf16(acc, sx, sw))[0, 0]
+        assert abs(y - c * d) <= abs(c * d) * (2.0 ** -8 + 4 * U)
+
+
+# ------------------------------------------------------------------ epilogues
+
+def test_dequant_against_fp64():
+    """fp32 dequant (acc * s_x) * s_w is within 3 roundings of the exact
+    product, and its bf16 is within one bf16 ulp; scales apply per row (s_x)
+    and per column (s_w), not the other way round (O8)."""
+    rng = np.random.default_rng(21)
+    acc = rng.integers(-2 ** 28, 2 ** 28, (9, 11)).astype(np.int32)
+    sx = rng.uniform(0.001, 2, 9).astype(np.float32)
+    sw = rng.uniform(0.0001, 0.01, 11).astype(np.float32)
+    f = oracle.dequant_f32(acc, sx, sw).astype(np.float64)
+    exact = acc.astype(np.float64) * sx.astype(np.float64)[:, None] * sw.astype(np.float64)[None, :]
+    assert np.all(np.abs(f - exact) <= 3.01 * U * np.abs(exact))
+    y = hd.bf16_bits_to_f64(oracle.dequant_bf16(acc, sx, sw))
+    assert np.all(np.abs(y - exact) <= np.abs(exact) * (2.0 ** -8 + 4 * U))
+
+
+def test_exp_against_exact():
+    """The fixed fp32 exponential is within 1 ulp of the exact e^x over
+    [-86, 88.7], exact at 0, +inf above the fp32 range, 0 below -86."""
+    xs = np.concatenate([np.linspace(-86, 88.7, 40001), np.linspace(-1, 1, 4001)]).astype(np.float32)
+    worst = 0.0
+    for x in xs:
+        e = oracle.exp(float(x))
+        t = math.exp(float(x))
+        worst = max(worst, abs(e - t) / float(np.spacing(np.float32(t))))
+    assert worst <= 1.0, worst
+    assert oracle.exp(0.0) == 1.0
+    assert oracle.exp(89.0) == math.inf and oracle.exp(-90.0) == 0.0
+
+
+def test_silu_special_values_and_accuracy():
+    """silu(0) = 0, silu(g) -> -0 for very negative g, silu(g) = g for large g,
+    and elsewhere within 3 * 2^-23 relative of the exact g * sigmoid(g) (exp
+    within 1 ulp, then three RNE roundings: the add, the division, and none
+    else)."""
+    assert oracle.silu(0.0) == 0.0
+    v = oracle.silu(-100.0)
+    assert v == 0.0 and math.copysign(1.0, v) < 0
+    assert oracle.silu(100.0) == 100.0
+    for g in np.linspace(-60, 60, 6001).astype(np.float32):
+        g = float(g)
+        t = g / (1 + math.exp(-g))
+        if t == 0:
+            continue
+        assert abs(oracle.silu(g) - t) <= 3 * 2.0 ** -23 * abs(t), g
+
+
+def test_bf16_rounding_matches_torch():
+    """The oracle's fp32 -> bf16 rounding equals torch's cast (round half to
+    even) on random values, exact ties, overflow and signed zeros (O10)."""
+    rng = np.random.default_rng(22)
+    f = (rng.standard_normal(20000) * np.exp2(rng.integers(-100, 100, 20000))).astype(np.float32)
+    ties = np.array([0x3F808000, 0x3F818000, 0xBF808000, 0x3F80FFFF, 0x7F7FFFFF, 0x00000000,
+                     0x80000000, 0x00018000, 0x7F800000], np.uint32).view(np.float32)
+    f = np.concatenate([f, ties])
+    assert np.array_equal(oracle.f32_to_bf16(f), workloads.to_bf16_bits(f))
+    b = oracle.f32_to_bf16(np.array([np.nan], np.float32))[0]
+    assert (b & 0x7F80) == 0x7F80 and (b & 0x7F) != 0
+
+
+def test_swiglu_epilogue_layout_and_value():
+    """SwiGLU takes the gate from the first half of the columns and the up
+    projection from the second; y = bf16(silu(g) * u) within one bf16 ulp of
+    the exact value (O9, S13)."""
+    rng = np.random.default_rng(23)
+    i = 24
+    acc = rng.integers(-3_000_000, 3_000_000, (5, 2 * i)).astype(np.int32)
+    sx = rng.uniform(0.01, 0.1, 5).astype(np.float32)
+    sw = rng.uniform(1e-5, 1e-4, 2 * i).astype(np.float32)
+    y = hd.bf16_bits_to_f64(oracle.swiglu_bf16(acc, sx, sw))
+    g = acc[:, :i] * sx.astype(np.float64)[:, None] * sw[:i].astype(np.float64)
+    u = acc[:, i:] * sx.astype(np.float64)[:, None] * sw[i:].astype(np.float64)
+    exact = g / (1 + np.exp(-g)) * u
+    assert np.all(np.abs(y - exact) <= np.abs(exact) * (2.0 ** -8 + 16 * U) + 1e-30)
+    swapped = u / (1 + np.exp(-u)) * g
+    assert not np.allclose(y, swapped, rtol=1e-2)
+
+
+# ------------------------------------------------------------------ method level
+
+def _rel_fro(y_bits, exact):
+    y = hd.bf16_bits_to_f64(y_bits)
+    return np.linalg.norm(y - exact) / np.linalg.norm(exact)
+
+
+@pytest.mark.parametrize("cid,rows", [(1, None), (2, 48)])
+def test_rotation_beats_unrotated_int8(cid, rows):
+    """The method's claim (RESEARCH.md, "Weight families"): on inputs with
+    outlier channels the rotated int8 product is far closer to x W^T than
+    per-token int8 without rotation (same oracle with H replaced by I) (C12)."""
+    d = workloads.make_linear(cid, m=rows)
+    x = hd.bf16_bits_to_f64(d["x"])
+    exact = x @ d["w"].astype(np.float64).T
+    qw, sw = oracle.quantize_weight(d["w"])
+    y_rot = oracle.linear_rows(d["x"], qw, sw)
+    qx0, sx0 = oracle.quantize_rows(x.astype(np.float32))
+    qw0, sw0 = oracle.quantize_rows(d["w"])
+    y_plain = oracle.dequant_bf16(oracle.gemm_s32(qx0, qw0), sx0, sw0)
+    e_rot, e_plain = _rel_fro(y_rot, exact), _rel_fro(y_plain, exact)
+    assert e_rot < 0.5 * e_plain, (e_rot, e_plain)
+    assert e_rot < 0.05
+
+
+def test_determinism_across_thread_counts():
+    """Rows are independent, so results are identical for 1 and many threads (C13)."""
+    d = workloads.make_linear(1)
+    before = oracle.get_threads()
+    try:
+        oracle.set_threads(1)
+        a = oracle.quantize_weight(d["w"]), oracle.linear_rows(d["x"], *oracle.quantize_weight(d["w"]))
+        oracle.set_threads(8)
+        b = oracle.quantize_weight(d["w"]), oracle.linear_rows(d["x"], *oracle.quantize_weight(d["w"]))
+    finally:
+        oracle.set_threads(before)
+    assert np.array_equal(a[0][0], b[0][0]) and np.array_equal(a[0][1], b[0][1])
+    assert np.array_equal(a[1], b[1])
+
+
+def test_row_subset_equals_full():
+    """Processing a subset of rows gives exactly those rows of the full result
+    (what the full-size parity tests rely on)."""
+    d = workloads.make_linear(1)
+    qw, sw = oracle.quantize_weight(d["w"])
+    full = oracle.linear_rows(d["x"], qw, sw)
+    rows = np.array([63, 0, 17, 17, 40])
+    sub = oracle.linear_rows(d["x"], qw, sw, rows)
+    assert np.array_equal(sub, full[rows])
+
+
+def test_stage_order_is_ascending():
+    """The butterfly's stage order decides rounding (reading: spans 1, 2, ..., 128).
+    For x = (1, 2^-24, 2^-24, 0, ...) the ascending order gives, by hand,
+    16 * out[i] = (1, 1, 1 - 2^-24, 1 - 2^-23)[i & 3]; the descending order
+    would give (1, 1 - 2^-24, 1, 1 - 2^-23) and the exact transform
+    (1 + 2^-23, 1, 1, 1 - 2^-23)."""
+    x = np.zeros(256, np.float32)
+    x[0] = 1.0
+    x[1] = x[2] = 2.0 ** -24
+    got = oracle.fwht256(x).astype(np.float64) * 16
+    pattern = np.array([1.0, 1.0, 1.0 - 2.0 ** -24, 1.0 - 2.0 ** -23])
+    assert np.array_equal(got, pattern[np.arange(256) & 3])
+
+
+def _division_cases():
+    # (amax, v) pairs, bf16-exact, where rint(v / s) with a correctly rounded
+    # quotient differs from rint(v * RN(1/s)); found by a seeded search and
+    # checked below with exact rationals.
+    return [(56.25, -28.125), (61.0, 30.5), (44.75, 22.375), (9.8125, -4.90625),
+            (3.765625, -1.8828125), (43.75, 21.875), (19.5, 9.75), (19.5, -9.75)]
+
+
+def _expected_code(amax, v):
+    from fractions import Fraction
+    s = hd.rn_f32(Fraction(amax) / 127)
+    q = hd.rint_half_even(hd.rn_f32(Fraction(v) / Fraction(s)))
+    recip = hd.rn_f32(1 / Fraction(s))
+    q_recip = hd.rint_half_even(hd.rn_f32(Fraction(v) * Fraction(recip)))
+    return s, q, q_recip
+
+
+@pytest.mark.parametrize("path", ["activation", "weight"])
+def test_quotient_is_correctly_rounded(path):
+    """Codes use a correctly rounded v / s (reading of the absmax quantizer),
+    not v times a rounded reciprocal.  Rows are built so that their rotation is
+    exactly (amax at one position, v at another); the expected code comes from
+    exact rational arithmetic.  Each case is one where the two differ."""
+    H = hd.H().astype(np.float64)
+    cases = _division_cases()
+    rows, want_s, want_q = [], [], []
+    for (amax, v) in cases:
+        s, q, q_recip = _expected_code(amax, v)
+        assert q != q_recip
+        row = np.zeros(512)
+        row[0:256] = amax * H[:, 3] / 16
+        row[256:512] = v * H[:, 77] / 16
+        rows.append(row)
+        want_s.append(s)
+        want_q.append(q)
+    rows = np.array(rows)
+    if path == "activation":
+        assert hd.is_bf16_exact(rows)
+        q, s = oracle.rotate_quant_act(workloads.to_bf16_bits(rows.astype(np.float32)))
+    else:
+        q, s = oracle.quantize_weight(rows.astype(np.float32))
+    assert np.array_equal(s.astype(np.float64), np.array(want_s))
+    assert np.array_equal(q[:, 3].astype(np.int64), np.full(len(cases), 127))
+    assert np.array_equal(q[:, 256 + 77].astype(np.int64), np.array(want_q))
+    assert np.count_nonzero(q) == 2 * len(cases)
+
+
+def _golden(tag):
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "closed_forms.txt")
+    out = []
+    for line in open(path):
+        parts = line.split()
+        if parts and parts[0] == tag:
+            out.append(parts[1:])
+    assert out, tag
+    return out
+
+
+def test_golden_closed_forms():
+    """The stored closed-form table (tests/golden/closed_forms.txt) holds for
+    the oracle: half-even ties, int32 extremes and the stage-order pattern."""
+    rng = np.random.default_rng(24)
+    for v, code in _golden("ties"):
+        x, rot = _tie_row(512, 1.0, rng, [127.0, float(v)])
+        q, s = oracle.rotate_quant_act(workloads.to_bf16_bits(x[None].astype(np.float32)))
+        assert s[0] == 1.0
+        assert int(q[0, 256 + np.nonzero(rot[256:])[0][0]]) == int(code)
+    for k, a, b, want in _golden("gemm"):
+        k = int(k)
+        qa = np.full((1, k), int(a), np.int8)
+        qb = np.full((1, k), int(b), np.int8)
+        assert oracle.gemm_s32(qa, qb)[0, 0] == int(want)
+    x = np.zeros(256, np.float32)
+    x[0] = 1.0
+    x[1] = x[2] = 2.0 ** -24
+    got = oracle.fwht256(x).astype(np.float64) * 16
+    for i, val in _golden("stage"):
+        assert np.all(got[np.arange(256) % 4 == int(i)] == float(val))
+
+
+def test_cfg1_digest_unchanged():
+    """The oracle's tiny-config results match the committed digests (a lock
+    against unintended changes of its arithmetic or of the input generator)."""
+    from tests.golden.make_cfg1_digest import digests
+    import os
+    path = os.path.join(os.path.dirname(__file__), "golden", "cfg1_oracle_digest.txt")
+    want = dict(l.split() for l in open(path) if l.strip() and not l.startswith("#"))
+    assert digests() == want
