@@ -1,0 +1,237 @@
+"""Benchmark of the ConvRot int8 quantized linear on one MI355X.
+
+One step is one pass of the whole hot path over one batch: the FFN of one
+MiniMax H3 DiT block at 32256 tokens (hidden 5376, FFN width 14336):
+    x [32256, 5376] bf16 --rotate+quant--> codes --int8 GEMM + SwiGLU--> h [32256, 14336] bf16
+    h --rotate+quant--> codes --int8 GEMM + dequant--> y [32256, 5376] bf16
+(the FFN-up configuration with its Laplace activations, chained into the
+FFN-down weights).  Weights are rotated and quantized once, before timing
+(load-time; they stay quantized in memory); that step is timed separately.
+
+Printed: one JSON line with whole-step effective TOPS (2 M N K summed over
+both GEMMs / step time), the roofline of the dominant kernel (the fused
+SwiGLU GEMM, against the dense int8 MFMA peak), and the CPU oracle timed on a
+bounded sample of the same step.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "ConvRot int8 linear effective TOPS + % of int8 MFMA peak (hidden 5376 FFN)"
+PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def make_down_weight():
+    """W_down [5376, 14336] exactly as the FFN-down config draws it."""
+    import workloads
+    c4 = workloads.CONFIGS[4]
+    rng = np.random.default_rng(c4.seed)
+    # skip the two activation draws of that config without materialising them
+    for _ in range(2):
+        for r0 in range(0, c4.m, 4096):
+            rng.standard_normal((min(4096, c4.m - r0), c4.k), dtype=np.float32)
+    w = rng.standard_normal((c4.n, c4.k), dtype=np.float32)
+    w *= np.float32(0.01)
+    return w
+
+
+def cpu_baseline(x_bits, w_up, w_dn, target_s=12.0):
+    """The CPU oracle (as it stands) on a bounded sample of the same step:
+    the first R token rows through both layers."""
+    import oracle
+    threads = oracle.get_threads()
+    log("cpu baseline: oracle weight prep (untimed)")
+    qwu, swu = oracle.quantize_weight(w_up)
+    qwd, swd = oracle.quantize_weight(w_dn)
+    n_up, k_up = qwu.shape
+    n_dn, k_dn = qwd.shape
+
+    def run(rows):
+        t0 = time.perf_counter()
+        h = oracle.linear_swiglu_rows(x_bits[:rows], qwu, swu)
+        oracle.linear_rows(h, qwd, swd)
+        return time.perf_counter() - t0
+
+    r = 4
+    t = run(r)
+    rows = max(4, min(512, int(r * target_s / max(t, 1e-3))))
+    log("cpu baseline: %d rows (probe %d rows took %.2f s)" % (rows, r, t))
+    t = run(rows)
+    ops = 2.0 * rows * (n_up * k_up + n_dn * k_dn)
+    return {"value": ops / t / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
+            "sample": "first %d of 32256 token rows through FFN-up+SwiGLU and FFN-down "
+                      "(rotate+quantize, int32 GEMM, epilogues), %.1f s" % (rows, t)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--m", type=int, default=None, help="token rows (default 32256)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build runs the layer on a single MI355X "
+              "(token sharding across GPUs needs no exchange and is not launched here)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rotation_quantized_dit_amd as cr
+
+    cr.load_library()
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+    log("generating inputs")
+    t0 = time.perf_counter()
+    import workloads
+    up = workloads.make_linear(3, m=args.m)
+    x_bits, w_up = up["x"], up["w"]
+    w_dn = make_down_weight()
+    log("inputs ready in %.1f s" % (time.perf_counter() - t0))
+    M, K1 = x_bits.shape
+    N1 = w_up.shape[0]
+    I = N1 // 2
+    N2, K2 = w_dn.shape
+    assert K2 == I
+
+    x = torch.from_numpy(x_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    wu = torch.from_numpy(w_up).to(dev)
+    wd = torch.from_numpy(w_dn).to(dev)
+
+    # load-time weight quantization (timed on its own)
+    qwu, swu = cr.quantize_weight(wu)
+    qwd, swd = cr.quantize_weight(wd)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    cr.quantize_weight(wu, qwu, swu)
+    cr.quantize_weight(wd, qwd, swd)
+    e1.record()
+    torch.cuda.synchronize()
+    wq_ms = e0.elapsed_time(e1)
+    wq_bytes = 5.0 * (N1 * K1 + N2 * K2) + 4.0 * (N1 + N2)
+
+    # preallocated activations, codes and outputs: nothing is allocated in the timed region
+    qx1 = torch.empty((M, K1), dtype=torch.int8, device=dev)
+    sx1 = torch.empty((M,), dtype=torch.float32, device=dev)
+    h = torch.empty((M, I), dtype=torch.bfloat16, device=dev)
+    qx2 = torch.empty((M, K2), dtype=torch.int8, device=dev)
+    sx2 = torch.empty((M,), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N2), dtype=torch.bfloat16, device=dev)
+
+    def step(ev=None):
+        if ev:
+            ev[0].record()
+        cr.rotate_quant_act(x, qx1, sx1)
+        if ev:
+            ev[1].record()
+        cr.gemm_swiglu(qx1, sx1, qwu, swu, out=h)
+        if ev:
+            ev[2].record()
+        cr.rotate_quant_act(h, qx2, sx2)
+        if ev:
+            ev[3].record()
+        cr.gemm_dequant(qx2, sx2, qwd, swd, out=y)
+        if ev:
+            ev[4].record()
+
+    log("warmup %d" % args.warmup)
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    log("timing %d steps" % args.steps)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    seg = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(args.steps)])
+    step_ms = np.array([evs[i][0].elapsed_time(evs[i][4]) for i in range(args.steps)])
+    ms = float(step_ms.mean())
+    ops_up = 2.0 * M * N1 * K1
+    ops_dn = 2.0 * M * N2 * K2
+    total_ops = ops_up + ops_dn
+    value = total_ops / (ms * 1e-3) / 1e12
+
+    rot1_b = 3.0 * M * K1 + 4.0 * M
+    rot2_b = 3.0 * M * K2 + 4.0 * M
+    kern = {}
+    names = ["rotate_quant_up", "gemm_swiglu_up", "rotate_quant_down", "gemm_dequant_down"]
+    for j, name in enumerate(names):
+        d = float(seg[:, j].mean())
+        e = {"ms": round(d, 4)}
+        if name.startswith("rotate"):
+            b = rot1_b if j == 0 else rot2_b
+            e["GB/s"] = round(b / (d * 1e-3) / 1e9, 1)
+            e["pct_hbm_peak"] = round(100.0 * b / (d * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
+        else:
+            o = ops_up if j == 1 else ops_dn
+            e["TOPS"] = round(o / (d * 1e-3) / 1e12, 1)
+            e["pct_int8_peak"] = round(100.0 * o / (d * 1e-3) / 1e12 / PEAK_INT8_TOPS, 1)
+        kern[name] = e
+
+    # cross-check: the same step through the fused entry points (same kernels)
+    torch.cuda.synchronize()
+    ws = torch.empty(max(cr.workspace_bytes(M, K1), cr.workspace_bytes(M, K2)), dtype=torch.uint8, device=dev)
+    f0, f1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f0.record()
+    for _ in range(args.steps):
+        cr.linear_swiglu(x, qwu, swu, out=h, workspace=ws)
+        cr.linear(h, qwd, swd, out=y, workspace=ws)
+    f1.record()
+    torch.cuda.synchronize()
+    fused_ms = f0.elapsed_time(f1) / args.steps
+
+    d_up = kern["gemm_swiglu_up"]["ms"]
+    roofline = {"kernel": "gemm_swiglu_up (int8 MFMA GEMM + SwiGLU epilogue)", "bound": "mfma",
+                "achieved": round(ops_up / (d_up * 1e-3) / 1e12, 1), "peak": PEAK_INT8_TOPS,
+                "unit": "TOP/s", "frac": round(ops_up / (d_up * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
+                "traffic": None,
+                "per_launch_ops": ops_up}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(x_bits, w_up, w_dn)
+
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TOPS", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "int8",
+        "data": "synthetic",
+        "config": {"workload": "ffn_block: FFN-up+SwiGLU then FFN-down of one H3 DiT block",
+                   "tokens": M, "hidden": K1, "ffn": I, "gemms": ["%dx%dx%d" % (M, N1, K1),
+                                                                  "%dx%dx%d" % (M, N2, K2)]},
+        "pct_int8_peak": round(100.0 * value / PEAK_INT8_TOPS, 2),
+        "kernels": kern,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "fused_api_ms_per_step": round(fused_ms, 4),
+        "weight_quant": {"ms": round(wq_ms, 4), "GB/s": round(wq_bytes / (wq_ms * 1e-3) / 1e9, 1)},
+        "wall_s": round(wall, 3),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

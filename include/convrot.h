@@ -1,0 +1,155 @@
+/*
+ * convrot.h -- C ABI of the ConvRot int8 quantized linear for AMD Instinct
+ * MI355X (gfx950).
+ *
+ * The layer (MiniMax H3 DiT projections, hidden size 5376):
+ *   1. rotate each activation row along K with the orthonormal Hadamard of
+ *      size 256, group by group (cloud-worker docs/RESEARCH.md, "Weight
+ *      families": ConvRot is a group-wise Hadamard rotation written as a
+ *      convolution, which spreads activation outliers; h3-rs README, model
+ *      file table: "Hadamard-256");
+ *   2. quantize the rotated row to int8 with one symmetric scale per token
+ *      (h3-rs README, "Speed": the fused GEMM quantizes activations per row and
+ *      the rotation runs inside that quantizer);
+ *   3. contract with int8 weights that were rotated the same way and quantized
+ *      with one scale per output row, accumulating in int32 (h3-rs README,
+ *      model file table: "int8 per-row"; quantized weights stay quantized in
+ *      memory);
+ *   4. rescale by both scales and write bf16 (h3-rs README, "Speed": the GEMM
+ *      writes bf16 directly), optionally applying SwiGLU to paired gate/up rows
+ *      in the same epilogue (h3-rs README, "Speed": fc1's gate/up rows are
+ *      paired so SwiGLU fuses into the epilogue; Minimax_h3_hybrid model card,
+ *      "Checkpoints": int8 ConvRot keeps the fused SwiGLU path).
+ *
+ * Exact definitions, as computed:
+ *   rotation   v = x . blockdiag(H/16), H[i][j] = (-1)^popcount(i & j), over
+ *              contiguous groups of 256; fp32 butterfly with spans 1, 2, ...,
+ *              128 in that order, each step one RNE add or subtract, then * 1/16;
+ *   scale      s = max_k |v_k| / 127 (correctly rounded fp32);
+ *   codes      q_k = rint(v_k / s) with a correctly rounded quotient and round
+ *              half to even; s == 0 gives all-zero codes;
+ *   contract   acc[m][n] = sum_k q_x[m][k] * q_w[n][k] (exact int32);
+ *   dequant    y = bf16_rne(((float)acc * s_x[m]) * s_w[n]);
+ *   SwiGLU     g, u = the fp32 dequant of gate column j and up column i + j;
+ *              y = bf16_rne(silu(g) * u), silu(g) = g / (1 + exp(-g)) with one
+ *              fixed fp32 exp (Cody-Waite reduction with ln2 split into
+ *              0x1.62e4p-1 + 0x1.7f7d1cp-20, k = rint(x * 0x1.715476p+0), degree-7
+ *              Taylor polynomial in Horner form with fused multiply-adds, scaled
+ *              by 2^k; exp(x) = +inf for x > 88.72 and 0 for x < -86).
+ * All results are bit-reproducible: the same inputs give the same bytes on
+ * every call, launch shape and device of this architecture.
+ *
+ * Conventions for every entry point:
+ *   - All array pointers are DEVICE pointers, owned by the caller.  The library
+ *     never allocates, frees, synchronizes, or changes the current device.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t passed as
+ *     void*; NULL is the default stream) on the current device.
+ *   - Arrays are dense and row-major (leading dimension = last extent).
+ *     bf16 travels as its raw 16-bit pattern (uint16_t).
+ *   - Every pointer must be 16-byte aligned.
+ *   - k must be a positive multiple of 256 and at most 133120 (so that
+ *     127 * 127 * k < 2^31: the int32 accumulator cannot overflow).
+ *   - m == 0 or n == 0 (i == 0) is success with no work enqueued; sizes are
+ *     checked first, so an empty call may pass NULL pointers.
+ *   - Argument errors are detected on the host before anything is enqueued and
+ *     leave all memory untouched.  A failed launch returns CONVROT_ERR_LAUNCH
+ *     (this includes a device that is not gfx950).  Faults during execution
+ *     surface at the caller's next synchronization.  Nothing aborts and no C++
+ *     exception crosses the ABI.
+ *   - Outputs must not overlap inputs.  Non-finite inputs give unspecified
+ *     outputs.
+ *   - The library keeps no state; calls are thread-safe and reentrant.
+ */
+#ifndef CONVROT_H
+#define CONVROT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+    CONVROT_OK = 0,
+    CONVROT_ERR_NULL = 1,      /* a required pointer is NULL                      */
+    CONVROT_ERR_SHAPE = 2,     /* negative size, k % 256 != 0, k > 133120, ...   */
+    CONVROT_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned               */
+    CONVROT_ERR_WORKSPACE = 4, /* workspace NULL or smaller than required        */
+    CONVROT_ERR_LAUNCH = 5     /* the kernel launch failed (see hipGetLastError) */
+};
+
+#define CONVROT_GROUP 256
+#define CONVROT_MAX_K 133120
+
+/* Load-time weight preparation (h3-rs README, model file table: int8 per-row +
+ * ConvRot Hadamard-256; weights stay quantized in memory).
+ *   w    [n, k] fp32 input weight (rows = output channels)
+ *   q_w  [n, k] int8 output codes of the rotated rows
+ *   s_w  [n]    fp32 output per-row scales                                  */
+int convrot_quantize_weight(const float* w, int64_t n, int64_t k,
+                            int8_t* q_w, float* s_w, void* stream);
+
+/* Per-token activation rotation + quantization (h3-rs README, "Speed").
+ *   x    [m, k] bf16 input activations
+ *   q_x  [m, k] int8 output codes
+ *   s_x  [m]    fp32 output per-token scales                                */
+int convrot_rotate_quant_act(const uint16_t* x, int64_t m, int64_t k,
+                             int8_t* q_x, float* s_x, void* stream);
+
+/* Workspace that convrot_linear / convrot_linear_swiglu need for m tokens of
+ * length k: q_x at offset 0 (m * k bytes), then s_x at offset m * k (4 * m
+ * bytes; 256-byte aligned whenever the workspace is, since k % 256 == 0).
+ * Returns 0 for invalid sizes.                                               */
+size_t convrot_workspace_bytes(int64_t m, int64_t k);
+
+/* The ConvRot int8 linear: y = dequant(rotate_quant(x) . q_w^T) (h3-rs
+ * README, "Speed": fused int8 GEMM that quantizes activations per row and
+ * writes bf16 directly).
+ *   x          [m, k] bf16 activations
+ *   q_w, s_w   [n, k] int8 / [n] fp32 from convrot_quantize_weight
+ *   y          [m, n] bf16 output
+ *   workspace  >= convrot_workspace_bytes(m, k) bytes of device memory; on
+ *              return it holds this call's q_x and s_x (enqueued).          */
+int convrot_linear(const uint16_t* x, int64_t m, int64_t k,
+                   const int8_t* q_w, const float* s_w, int64_t n,
+                   uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The fc1 ConvRot linear with SwiGLU fused into its epilogue (h3-rs README,
+ * "Speed"; Minimax_h3_hybrid model card, "Checkpoints").
+ *   q_w, s_w   [2i, k] int8 / [2i] fp32: rows [0, i) are the gate projection,
+ *              rows [i, 2i) the up projection (quantize the whole [2i, k]
+ *              weight with convrot_quantize_weight; scales are per row, so this
+ *              equals quantizing the halves separately)
+ *   y          [m, i] bf16 output silu(gate) * up                            */
+int convrot_linear_swiglu(const uint16_t* x, int64_t m, int64_t k,
+                          const int8_t* q_w, const float* s_w, int64_t i,
+                          uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The contraction with its bf16 dequant epilogue on codes prepared by the
+ * caller (the second half of convrot_linear).
+ *   q_x, s_x   [m, k] int8 / [m] fp32;  q_w, s_w  [n, k] int8 / [n] fp32
+ *   y          [m, n] bf16                                                   */
+int convrot_gemm_dequant(const int8_t* q_x, const float* s_x, const int8_t* q_w,
+                         const float* s_w, int64_t m, int64_t n, int64_t k,
+                         uint16_t* y, void* stream);
+
+/* The contraction with the SwiGLU epilogue on prepared codes (the second half
+ * of convrot_linear_swiglu).  q_w, s_w have 2i rows; y is [m, i] bf16.       */
+int convrot_gemm_swiglu(const int8_t* q_x, const float* s_x, const int8_t* q_w,
+                        const float* s_w, int64_t m, int64_t i, int64_t k,
+                        uint16_t* y, void* stream);
+
+/* The raw int32 accumulators of the same contraction (same main loop), for
+ * exact checks: acc [m, n] int32 = q_x . q_w^T.                              */
+int convrot_gemm_s32(const int8_t* q_x, const int8_t* q_w, int64_t m, int64_t n, int64_t k,
+                     int32_t* acc, void* stream);
+
+/* Static, NUL-terminated description of a status code (never NULL).         */
+const char* convrot_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CONVROT_H */

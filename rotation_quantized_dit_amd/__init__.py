@@ -1,0 +1,24 @@
+"""MI355X-native ConvRot int8 quantized linear (MiniMax H3 DiT projections).
+
+A group-wise Hadamard-256 rotation spreads activation outliers, activations are
+quantized to int8 per token and weights per row, the product is an int8 x int8
+-> int32 contraction on CDNA4 MFMA, and the result is rescaled to bf16 (with
+an optional fused SwiGLU).  The work runs in hand-written HIP kernels for
+gfx950 behind the C ABI of include/convrot.h; this package is its Python
+binding (torch provides device memory and the stream).
+"""
+from ._lib import (  # noqa: F401
+    GROUP,
+    MAX_K,
+    ConvRotError,
+    gemm_dequant,
+    gemm_s32,
+    gemm_swiglu,
+    linear,
+    linear_swiglu,
+    load_library,
+    quantize_weight,
+    rotate_quant_act,
+    status_string,
+    workspace_bytes,
+)

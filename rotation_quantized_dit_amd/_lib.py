@@ -1,0 +1,221 @@
+"""ctypes binding of libconvrot.so (the C ABI in include/convrot.h).
+
+Argument marshalling only: shapes, dtypes and devices are checked, outputs are
+allocated with torch (unless passed in), and torch's current HIP stream is
+handed to the library.  Every step of the computation runs in the library's
+HIP kernels; there is no fallback of any kind.  If the library is not built
+the first call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libconvrot.so")
+
+GROUP = 256
+MAX_K = 133120
+
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH = range(6)
+
+SYMBOLS = (
+    "convrot_quantize_weight", "convrot_rotate_quant_act", "convrot_workspace_bytes",
+    "convrot_linear", "convrot_linear_swiglu", "convrot_gemm_dequant", "convrot_gemm_swiglu",
+    "convrot_gemm_s32", "convrot_status_string",
+)
+
+
+class ConvRotError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__("%s failed with status %d: %s" % (fn, status, msg))
+        self.status = status
+
+
+_lock = threading.Lock()
+_lib = None
+
+
+def load_library() -> ctypes.CDLL:
+    """Load libconvrot.so (raises if it has not been built)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libconvrot.so is not built (%s); run "
+                               "`python -m rotation_quantized_dit_amd.build`" % LIB_PATH)
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, SZ, I = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t, ctypes.c_int
+        sig = {
+            "convrot_quantize_weight": ([P, I64, I64, P, P, P], I),
+            "convrot_rotate_quant_act": ([P, I64, I64, P, P, P], I),
+            "convrot_workspace_bytes": ([I64, I64], SZ),
+            "convrot_linear": ([P, I64, I64, P, P, I64, P, P, SZ, P], I),
+            "convrot_linear_swiglu": ([P, I64, I64, P, P, I64, P, P, SZ, P], I),
+            "convrot_gemm_dequant": ([P, P, P, P, I64, I64, I64, P, P], I),
+            "convrot_gemm_swiglu": ([P, P, P, P, I64, I64, I64, P, P], I),
+            "convrot_gemm_s32": ([P, P, I64, I64, I64, P, P], I),
+            "convrot_status_string": ([I], ctypes.c_char_p),
+        }
+        for name, (args, res) in sig.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+        return L
+
+
+def status_string(status: int) -> str:
+    return load_library().convrot_status_string(int(status)).decode()
+
+
+def workspace_bytes(m: int, k: int) -> int:
+    return int(load_library().convrot_workspace_bytes(int(m), int(k)))
+
+
+def _check(fn: str, st: int) -> None:
+    if st != OK:
+        raise ConvRotError(fn, st, status_string(st))
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if t.dim() != ndim:
+        raise ValueError("%s must have %d dims (got %s)" % (name, ndim, tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _out(out, shape, dtype, like: torch.Tensor, name: str) -> torch.Tensor:
+    if out is None:
+        return torch.empty(shape, dtype=dtype, device=like.device)
+    _dev(out, name, dtype, len(shape))
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(out.shape)))
+    return out
+
+
+def quantize_weight(w: torch.Tensor, q_w=None, s_w=None):
+    """fp32 W [n, k] -> (int8 codes [n, k], fp32 per-row scales [n]) of the rotated rows."""
+    _dev(w, "w", torch.float32, 2)
+    n, k = w.shape
+    q_w = _out(q_w, (n, k), torch.int8, w, "q_w")
+    s_w = _out(s_w, (n,), torch.float32, w, "s_w")
+    _check("convrot_quantize_weight", load_library().convrot_quantize_weight(
+        w.data_ptr(), n, k, q_w.data_ptr(), s_w.data_ptr(), _stream()))
+    return q_w, s_w
+
+
+def rotate_quant_act(x: torch.Tensor, q_x=None, s_x=None):
+    """bf16 x [m, k] -> (int8 codes [m, k], fp32 per-token scales [m])."""
+    _dev(x, "x", torch.bfloat16, 2)
+    m, k = x.shape
+    q_x = _out(q_x, (m, k), torch.int8, x, "q_x")
+    s_x = _out(s_x, (m,), torch.float32, x, "s_x")
+    _check("convrot_rotate_quant_act", load_library().convrot_rotate_quant_act(
+        x.data_ptr(), m, k, q_x.data_ptr(), s_x.data_ptr(), _stream()))
+    return q_x, s_x
+
+
+def _workspace(workspace, m, k, like):
+    need = max(workspace_bytes(m, k), 16)
+    if workspace is None:
+        return torch.empty(need, dtype=torch.uint8, device=like.device)
+    if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.dtype == torch.uint8
+            and workspace.is_contiguous()):
+        raise TypeError("workspace must be a contiguous uint8 GPU tensor")
+    return workspace
+
+
+def linear(x: torch.Tensor, q_w: torch.Tensor, s_w: torch.Tensor, out=None, workspace=None):
+    """ConvRot int8 linear: bf16 x [m, k] -> bf16 y [m, n]."""
+    _dev(x, "x", torch.bfloat16, 2)
+    _dev(q_w, "q_w", torch.int8, 2)
+    _dev(s_w, "s_w", torch.float32, 1)
+    m, k = x.shape
+    n = q_w.shape[0]
+    if q_w.shape[1] != k or s_w.shape[0] != n:
+        raise ValueError("shape mismatch: x %s, q_w %s, s_w %s" % (tuple(x.shape), tuple(q_w.shape), tuple(s_w.shape)))
+    y = _out(out, (m, n), torch.bfloat16, x, "out")
+    ws = _workspace(workspace, m, k, x)
+    _check("convrot_linear", load_library().convrot_linear(
+        x.data_ptr(), m, k, q_w.data_ptr(), s_w.data_ptr(), n, y.data_ptr(), ws.data_ptr(),
+        ws.numel(), _stream()))
+    return y
+
+
+def linear_swiglu(x: torch.Tensor, q_w: torch.Tensor, s_w: torch.Tensor, out=None, workspace=None):
+    """fc1 ConvRot linear with fused SwiGLU: q_w has 2i rows (gate then up); y is [m, i]."""
+    _dev(x, "x", torch.bfloat16, 2)
+    _dev(q_w, "q_w", torch.int8, 2)
+    _dev(s_w, "s_w", torch.float32, 1)
+    m, k = x.shape
+    n2 = q_w.shape[0]
+    if n2 % 2 or q_w.shape[1] != k or s_w.shape[0] != n2:
+        raise ValueError("shape mismatch: x %s, q_w %s, s_w %s" % (tuple(x.shape), tuple(q_w.shape), tuple(s_w.shape)))
+    i = n2 // 2
+    y = _out(out, (m, i), torch.bfloat16, x, "out")
+    ws = _workspace(workspace, m, k, x)
+    _check("convrot_linear_swiglu", load_library().convrot_linear_swiglu(
+        x.data_ptr(), m, k, q_w.data_ptr(), s_w.data_ptr(), i, y.data_ptr(), ws.data_ptr(),
+        ws.numel(), _stream()))
+    return y
+
+
+def _gemm_args(q_x, s_x, q_w, s_w):
+    _dev(q_x, "q_x", torch.int8, 2)
+    _dev(q_w, "q_w", torch.int8, 2)
+    if s_x is not None:
+        _dev(s_x, "s_x", torch.float32, 1)
+    if s_w is not None:
+        _dev(s_w, "s_w", torch.float32, 1)
+    m, k = q_x.shape
+    n, k2 = q_w.shape
+    if k != k2 or (s_x is not None and s_x.shape[0] != m) or (s_w is not None and s_w.shape[0] != n):
+        raise ValueError("shape mismatch")
+    return m, n, k
+
+
+def gemm_dequant(q_x, s_x, q_w, s_w, out=None):
+    """bf16 y [m, n] = bf16(((float)(q_x . q_w^T) * s_x) * s_w) on prepared codes."""
+    m, n, k = _gemm_args(q_x, s_x, q_w, s_w)
+    y = _out(out, (m, n), torch.bfloat16, q_x, "out")
+    _check("convrot_gemm_dequant", load_library().convrot_gemm_dequant(
+        q_x.data_ptr(), s_x.data_ptr(), q_w.data_ptr(), s_w.data_ptr(), m, n, k, y.data_ptr(),
+        _stream()))
+    return y
+
+
+def gemm_swiglu(q_x, s_x, q_w, s_w, out=None):
+    """bf16 y [m, i] = SwiGLU epilogue of the contraction with 2i weight rows."""
+    m, n2, k = _gemm_args(q_x, s_x, q_w, s_w)
+    if n2 % 2:
+        raise ValueError("q_w must have an even number of rows (gate then up)")
+    i = n2 // 2
+    y = _out(out, (m, i), torch.bfloat16, q_x, "out")
+    _check("convrot_gemm_swiglu", load_library().convrot_gemm_swiglu(
+        q_x.data_ptr(), s_x.data_ptr(), q_w.data_ptr(), s_w.data_ptr(), m, i, k, y.data_ptr(),
+        _stream()))
+    return y
+
+
+def gemm_s32(q_x, q_w, out=None):
+    """int32 acc [m, n] = q_x . q_w^T (raw accumulators of the same main loop)."""
+    m, n, k = _gemm_args(q_x, None, q_w, None)
+    acc = _out(out, (m, n), torch.int32, q_x, "out")
+    _check("convrot_gemm_s32", load_library().convrot_gemm_s32(
+        q_x.data_ptr(), q_w.data_ptr(), m, n, k, acc.data_ptr(), _stream()))
+    return acc

@@ -1,0 +1,161 @@
+// C ABI of the ConvRot int8 quantized linear (declared in include/convrot.h).
+//
+// This layer only validates arguments and enqueues the HIP kernels: every
+// step of the computation runs on the GPU.  Validation happens before any HIP
+// call, so argument errors never touch memory or the device.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/convrot.h"
+#include "kernels.h"
+
+namespace {
+
+using convrot::Epilogue;
+
+inline bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+// k: a positive multiple of the 256-element Hadamard group, small enough that
+// 127 * 127 * k fits int32.  Row counts must fit the launch grid (int32).
+inline int check_k(int64_t k) {
+    if (k <= 0 || (k % CONVROT_GROUP) != 0 || k > CONVROT_MAX_K) return CONVROT_ERR_SHAPE;
+    return CONVROT_OK;
+}
+
+inline int check_rows(int64_t r) {
+    if (r < 0 || r > (int64_t)INT32_MAX) return CONVROT_ERR_SHAPE;
+    return CONVROT_OK;
+}
+
+inline int launched(hipError_t e) { return e == hipSuccess ? CONVROT_OK : CONVROT_ERR_LAUNCH; }
+
+inline size_t ws_bytes(int64_t m, int64_t k) { return (size_t)m * (size_t)k + 4u * (size_t)m; }
+
+// Shape checks of the GEMM entry points.  n_rows_w is the number of weight
+// rows (n, or 2i for SwiGLU).
+int check_gemm_shape(int64_t m, int64_t n, int64_t n_rows_w, int64_t k) {
+    int st;
+    if ((st = check_rows(m)) || (st = check_rows(n)) || (st = check_rows(n_rows_w)) ||
+        (st = check_k(k)))
+        return st;
+    // the tile grid (256 tokens x at least 128 columns per workgroup) must fit one launch
+    if (((m + 255) / 256) * ((n + 127) / 128) > (int64_t)INT32_MAX) return CONVROT_ERR_SHAPE;
+    return CONVROT_OK;
+}
+
+// Pointer checks of the GEMM entry points (after the shape checks and the
+// zero-size early return, so empty calls may pass NULL).
+int check_gemm_ptrs(const void* q_x, const void* s_x, bool need_sx, const void* q_w,
+                    const void* s_w, bool need_sw, const void* out) {
+    if (!q_x || !q_w || !out || (need_sx && !s_x) || (need_sw && !s_w)) return CONVROT_ERR_NULL;
+    if (!aligned16(q_x) || !aligned16(q_w) || !aligned16(out) || (need_sx && !aligned16(s_x)) ||
+        (need_sw && !aligned16(s_w)))
+        return CONVROT_ERR_ALIGN;
+    return CONVROT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* convrot_status_string(int status) {
+    switch (status) {
+        case CONVROT_OK: return "ok";
+        case CONVROT_ERR_NULL: return "a required pointer is NULL";
+        case CONVROT_ERR_SHAPE:
+            return "invalid shape (negative size, k not a positive multiple of 256, or k > 133120)";
+        case CONVROT_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+        case CONVROT_ERR_WORKSPACE: return "workspace is NULL or smaller than convrot_workspace_bytes(m, k)";
+        case CONVROT_ERR_LAUNCH: return "kernel launch failed (is the device gfx950?)";
+        default: return "unknown status";
+    }
+}
+
+size_t convrot_workspace_bytes(int64_t m, int64_t k) {
+    if (check_rows(m) || check_k(k)) return 0;
+    return ws_bytes(m, k);
+}
+
+int convrot_quantize_weight(const float* w, int64_t n, int64_t k, int8_t* q_w, float* s_w,
+                            void* stream) {
+    int st;
+    if ((st = check_rows(n)) || (st = check_k(k))) return st;
+    if (n == 0) return CONVROT_OK;
+    if (!w || !q_w || !s_w) return CONVROT_ERR_NULL;
+    if (!aligned16(w) || !aligned16(q_w) || !aligned16(s_w)) return CONVROT_ERR_ALIGN;
+    return launched(convrot::launch_rotate_quant_f32(w, n, k, q_w, s_w, (hipStream_t)stream));
+}
+
+int convrot_rotate_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* q_x, float* s_x,
+                             void* stream) {
+    int st;
+    if ((st = check_rows(m)) || (st = check_k(k))) return st;
+    if (m == 0) return CONVROT_OK;
+    if (!x || !q_x || !s_x) return CONVROT_ERR_NULL;
+    if (!aligned16(x) || !aligned16(q_x) || !aligned16(s_x)) return CONVROT_ERR_ALIGN;
+    return launched(convrot::launch_rotate_quant_bf16(x, m, k, q_x, s_x, (hipStream_t)stream));
+}
+
+int convrot_gemm_s32(const int8_t* q_x, const int8_t* q_w, int64_t m, int64_t n, int64_t k,
+                     int32_t* acc, void* stream) {
+    int st = check_gemm_shape(m, n, n, k);
+    if (st) return st;
+    if (m == 0 || n == 0) return CONVROT_OK;
+    if ((st = check_gemm_ptrs(q_x, nullptr, false, q_w, nullptr, false, acc))) return st;
+    return launched(convrot::launch_gemm(Epilogue::S32, q_x, nullptr, q_w, nullptr, m, n, k, acc,
+                                         (hipStream_t)stream));
+}
+
+int convrot_gemm_dequant(const int8_t* q_x, const float* s_x, const int8_t* q_w, const float* s_w,
+                         int64_t m, int64_t n, int64_t k, uint16_t* y, void* stream) {
+    int st = check_gemm_shape(m, n, n, k);
+    if (st) return st;
+    if (m == 0 || n == 0) return CONVROT_OK;
+    if ((st = check_gemm_ptrs(q_x, s_x, true, q_w, s_w, true, y))) return st;
+    return launched(convrot::launch_gemm(Epilogue::BF16, q_x, s_x, q_w, s_w, m, n, k, y,
+                                         (hipStream_t)stream));
+}
+
+int convrot_gemm_swiglu(const int8_t* q_x, const float* s_x, const int8_t* q_w, const float* s_w,
+                        int64_t m, int64_t i, int64_t k, uint16_t* y, void* stream) {
+    if (i < 0 || i > (int64_t)INT32_MAX / 2) return CONVROT_ERR_SHAPE;
+    int st = check_gemm_shape(m, i, 2 * i, k);
+    if (st) return st;
+    if (m == 0 || i == 0) return CONVROT_OK;
+    if ((st = check_gemm_ptrs(q_x, s_x, true, q_w, s_w, true, y))) return st;
+    return launched(convrot::launch_gemm(Epilogue::SWIGLU, q_x, s_x, q_w, s_w, m, i, k, y,
+                                         (hipStream_t)stream));
+}
+
+static int linear_common(const uint16_t* x, int64_t m, int64_t k, const int8_t* q_w,
+                         const float* s_w, int64_t n, int64_t n_rows_w, uint16_t* y,
+                         void* workspace, size_t workspace_bytes, bool swiglu, void* stream) {
+    if (n < 0 || n > (int64_t)INT32_MAX / 2) return CONVROT_ERR_SHAPE;
+    int st;
+    if ((st = check_gemm_shape(m, n, n_rows_w, k))) return st;
+    if (m == 0 || n == 0) return CONVROT_OK;
+    if ((st = check_gemm_ptrs(x, nullptr, false, q_w, s_w, true, y))) return st;
+    if (!workspace || workspace_bytes < ws_bytes(m, k)) return CONVROT_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return CONVROT_ERR_ALIGN;
+    int8_t* q_x = (int8_t*)workspace;
+    float* s_x = (float*)((char*)workspace + (size_t)m * (size_t)k);
+    hipStream_t s = (hipStream_t)stream;
+    if (convrot::launch_rotate_quant_bf16(x, m, k, q_x, s_x, s) != hipSuccess) return CONVROT_ERR_LAUNCH;
+    return launched(convrot::launch_gemm(swiglu ? Epilogue::SWIGLU : Epilogue::BF16, q_x, s_x, q_w,
+                                         s_w, m, n, k, y, s));
+}
+
+int convrot_linear(const uint16_t* x, int64_t m, int64_t k, const int8_t* q_w, const float* s_w,
+                   int64_t n, uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
+    return linear_common(x, m, k, q_w, s_w, n, n, y, workspace, workspace_bytes, false, stream);
+}
+
+int convrot_linear_swiglu(const uint16_t* x, int64_t m, int64_t k, const int8_t* q_w,
+                          const float* s_w, int64_t i, uint16_t* y, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+    if (i < 0 || i > (int64_t)INT32_MAX / 2) return CONVROT_ERR_SHAPE;
+    return linear_common(x, m, k, q_w, s_w, i, 2 * i, y, workspace, workspace_bytes, true, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,24 @@
+// Internal launchers shared by the C-ABI layer and the HIP kernels.
+// Every launcher assumes its arguments were validated by convrot_api.cpp.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace convrot {
+
+// K-ROT: group-wise Hadamard-256 rotation + per-row absmax int8 quantization.
+hipError_t launch_rotate_quant_bf16(const uint16_t* x, int64_t rows, int64_t k, int8_t* q,
+                                    float* s, hipStream_t stream);
+hipError_t launch_rotate_quant_f32(const float* x, int64_t rows, int64_t k, int8_t* q,
+                                   float* s, hipStream_t stream);
+
+// K-GEMM: int8 x int8 -> int32 on MFMA with one of three epilogues.
+enum class Epilogue { S32, BF16, SWIGLU };
+
+// For Epilogue::SWIGLU, n is the output width i and q_w / s_w hold 2i rows.
+hipError_t launch_gemm(Epilogue ep, const int8_t* q_x, const float* s_x, const int8_t* q_w,
+                       const float* s_w, int64_t m, int64_t n, int64_t k, void* out,
+                       hipStream_t stream);
+
+}  // namespace convrot

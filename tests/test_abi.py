@@ -1,0 +1,155 @@
+"""The C ABI loads, exports what include/convrot.h declares, and rejects bad
+arguments on the host before anything touches a device (CPU only: every call
+here fails validation or is a zero-size no-op, so no HIP call is made)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "convrot.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from rotation_quantized_dit_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        from rotation_quantized_dit_amd import build
+        build.build()
+    return _lib.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(convrot_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for must in ("convrot_quantize_weight", "convrot_rotate_quant_act", "convrot_linear",
+                 "convrot_linear_swiglu"):
+        assert must in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    from rotation_quantized_dit_amd import _lib
+    names = declared_functions()
+    assert sorted(_lib.SYMBOLS) == names
+    for n in names:
+        assert hasattr(L, n), n
+    # and exports them with C linkage (unmangled), nothing else named convrot_
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted(set(re.findall(r"\bT (convrot_\w+)$", out, flags=re.M)))
+    assert exported == names
+
+
+def test_status_strings(L):
+    from rotation_quantized_dit_amd import _lib
+    for st in range(6):
+        s = _lib.status_string(st)
+        assert isinstance(s, str) and s
+    assert _lib.status_string(0) == "ok"
+    assert "unknown" in _lib.status_string(99)
+
+
+def test_workspace_bytes(L):
+    assert L.convrot_workspace_bytes(32256, 5376) == 32256 * 5376 + 4 * 32256
+    assert L.convrot_workspace_bytes(0, 256) == 0
+    assert L.convrot_workspace_bytes(10, 255) == 0
+    assert L.convrot_workspace_bytes(-1, 256) == 0
+    assert L.convrot_workspace_bytes(1, 133120) == 133120 + 4
+    assert L.convrot_workspace_bytes(1, 133376) == 0
+
+
+A = 0x10000        # aligned fake device addresses: never dereferenced, validation fails first
+B = 0x20000
+C = 0x30000
+D = 0x40000
+MIS = 0x10008
+
+
+def test_k_bounds(L):
+    """k must be a positive multiple of 256 and at most 133120 (127^2 k < 2^31)."""
+    from rotation_quantized_dit_amd._lib import ERR_SHAPE
+    for k in (0, -256, 100, 257, 133376, 1 << 20):
+        assert L.convrot_rotate_quant_act(A, 4, k, B, C, None) == ERR_SHAPE, k
+        assert L.convrot_quantize_weight(A, 4, k, B, C, None) == ERR_SHAPE, k
+        assert L.convrot_gemm_s32(A, B, 4, 4, k, C, None) == ERR_SHAPE, k
+        assert L.convrot_linear(A, 4, k, B, C, 4, D, A, 1 << 30, None) == ERR_SHAPE, k
+
+
+def test_negative_sizes(L):
+    from rotation_quantized_dit_amd._lib import ERR_SHAPE
+    assert L.convrot_rotate_quant_act(A, -1, 256, B, C, None) == ERR_SHAPE
+    assert L.convrot_quantize_weight(A, -5, 256, B, C, None) == ERR_SHAPE
+    assert L.convrot_gemm_s32(A, B, -1, 4, 256, C, None) == ERR_SHAPE
+    assert L.convrot_gemm_s32(A, B, 4, -1, 256, C, None) == ERR_SHAPE
+    assert L.convrot_gemm_dequant(A, B, C, D, 4, -1, 256, A, None) == ERR_SHAPE
+    assert L.convrot_gemm_swiglu(A, B, C, D, 4, -1, 256, A, None) == ERR_SHAPE
+    assert L.convrot_linear(A, 4, 256, B, C, -1, D, A, 1 << 20, None) == ERR_SHAPE
+    assert L.convrot_linear_swiglu(A, 4, 256, B, C, -3, D, A, 1 << 20, None) == ERR_SHAPE
+    assert L.convrot_rotate_quant_act(A, 1 << 32, 256, B, C, None) == ERR_SHAPE
+
+
+def test_null_pointers(L):
+    from rotation_quantized_dit_amd._lib import ERR_NULL
+    assert L.convrot_rotate_quant_act(None, 4, 256, B, C, None) == ERR_NULL
+    assert L.convrot_rotate_quant_act(A, 4, 256, None, C, None) == ERR_NULL
+    assert L.convrot_rotate_quant_act(A, 4, 256, B, None, None) == ERR_NULL
+    assert L.convrot_quantize_weight(A, 4, 256, B, None, None) == ERR_NULL
+    assert L.convrot_gemm_s32(None, B, 4, 4, 256, C, None) == ERR_NULL
+    assert L.convrot_gemm_s32(A, B, 4, 4, 256, None, None) == ERR_NULL
+    assert L.convrot_gemm_dequant(A, None, C, D, 4, 4, 256, A, None) == ERR_NULL
+    assert L.convrot_gemm_dequant(A, B, C, None, 4, 4, 256, A, None) == ERR_NULL
+    assert L.convrot_gemm_swiglu(A, B, None, D, 4, 4, 256, A, None) == ERR_NULL
+    assert L.convrot_linear(A, 4, 256, B, None, 4, D, A, 1 << 20, None) == ERR_NULL
+    assert L.convrot_linear_swiglu(A, 4, 256, B, C, 4, None, A, 1 << 20, None) == ERR_NULL
+
+
+def test_alignment(L):
+    from rotation_quantized_dit_amd._lib import ERR_ALIGN
+    assert L.convrot_rotate_quant_act(MIS, 4, 256, B, C, None) == ERR_ALIGN
+    assert L.convrot_rotate_quant_act(A, 4, 256, B + 1, C, None) == ERR_ALIGN
+    assert L.convrot_quantize_weight(A, 4, 256, B, C + 4, None) == ERR_ALIGN
+    assert L.convrot_gemm_s32(A, B + 2, 4, 4, 256, C, None) == ERR_ALIGN
+    assert L.convrot_gemm_dequant(A, B, C, D, 4, 4, 256, A + 8, None) == ERR_ALIGN
+    assert L.convrot_linear(A, 4, 256, B, C, 4, D, MIS, 1 << 20, None) == ERR_ALIGN
+
+
+def test_workspace_checks(L):
+    from rotation_quantized_dit_amd._lib import ERR_WORKSPACE
+    need = L.convrot_workspace_bytes(4, 256)
+    assert L.convrot_linear(A, 4, 256, B, C, 4, D, None, need, None) == ERR_WORKSPACE
+    assert L.convrot_linear(A, 4, 256, B, C, 4, D, A, need - 1, None) == ERR_WORKSPACE
+    assert L.convrot_linear_swiglu(A, 4, 256, B, C, 4, D, A, need - 1, None) == ERR_WORKSPACE
+
+
+def test_zero_sizes_are_noops(L):
+    """m == 0 or n == 0 succeed without launching (safe with fake pointers)."""
+    from rotation_quantized_dit_amd._lib import OK
+    assert L.convrot_rotate_quant_act(A, 0, 256, B, C, None) == OK
+    assert L.convrot_quantize_weight(A, 0, 512, B, C, None) == OK
+    assert L.convrot_gemm_s32(A, B, 0, 4, 256, C, None) == OK
+    assert L.convrot_gemm_s32(A, B, 4, 0, 256, C, None) == OK
+    assert L.convrot_gemm_dequant(A, B, C, D, 0, 4, 256, A, None) == OK
+    assert L.convrot_gemm_swiglu(A, B, C, D, 4, 0, 256, A, None) == OK
+    assert L.convrot_linear(A, 0, 256, B, C, 4, D, None, 0, None) == OK
+    assert L.convrot_linear_swiglu(A, 7, 256, B, C, 0, D, None, 0, None) == OK
+    # empty calls may pass NULL (torch's empty tensors do), but bad shapes still fail
+    assert L.convrot_rotate_quant_act(None, 0, 256, None, None, None) == OK
+    assert L.convrot_gemm_s32(None, None, 0, 0, 256, None, None) == OK
+    assert L.convrot_linear(None, 0, 512, None, None, 9, None, None, 0, None) == OK
+    assert L.convrot_rotate_quant_act(None, 0, 300, None, None, None) != OK
+
+
+def test_python_binding_rejects_cpu_tensors():
+    import torch
+    import rotation_quantized_dit_amd as cr
+    with pytest.raises(ValueError):
+        cr.rotate_quant_act(torch.zeros(4, 256, dtype=torch.bfloat16))
+    with pytest.raises((TypeError, ValueError)):
+        cr.quantize_weight(torch.zeros(4, 256, dtype=torch.float64))

@@ -1,0 +1,231 @@
+"""GPU parity on small and edge-case inputs: the HIP library (through the C
+ABI) against the CPU oracle on the same seeded bytes.  Codes, scales and int32
+accumulators must match bit for bit; bf16 outputs must meet the 1e-2 relative
+bound and, since both sides evaluate the same rounding sequence, match bit for
+bit too."""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import gpu_util as gu
+from tests import hadamard as hd
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cr():
+    import rotation_quantized_dit_amd as cr
+    cr.load_library()
+    return cr
+
+
+def _f32_bits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def run_all_stages(cr, x_bits, w, swiglu=False):
+    """Every entry point on one input; returns GPU results and oracle results."""
+    import torch
+    xd, wd = gu.dev_bf16(x_bits), gu.dev(w)
+    qw_d, sw_d = cr.quantize_weight(wd)
+    qx_d, sx_d = cr.rotate_quant_act(xd)
+    acc_d = cr.gemm_s32(qx_d, qw_d)
+    if swiglu:
+        y_d = cr.linear_swiglu(xd, qw_d, sw_d)
+        y2_d = cr.gemm_swiglu(qx_d, sx_d, qw_d, sw_d)
+    else:
+        y_d = cr.linear(xd, qw_d, sw_d)
+        y2_d = cr.gemm_dequant(qx_d, sx_d, qw_d, sw_d)
+    torch.cuda.synchronize()
+    g = dict(q_w=gu.host(qw_d), s_w=gu.host(sw_d), q_x=gu.host(qx_d), s_x=gu.host(sx_d),
+             acc=gu.host(acc_d), y=gu.host_bf16(y_d), y2=gu.host_bf16(y2_d))
+    qw, sw = oracle.quantize_weight(w)
+    qx, sx = oracle.rotate_quant_act(x_bits)
+    acc = oracle.gemm_s32(qx, qw)
+    y = oracle.swiglu_bf16(acc, sx, sw) if swiglu else oracle.dequant_bf16(acc, sx, sw)
+    o = dict(q_w=qw, s_w=sw, q_x=qx, s_x=sx, acc=acc, y=y)
+    return g, o
+
+
+def check_all(g, o, what):
+    gu.assert_equal(g["q_w"], o["q_w"], what + " q_w")
+    gu.assert_equal(_f32_bits(g["s_w"]), _f32_bits(o["s_w"]), what + " s_w")
+    gu.assert_equal(g["q_x"], o["q_x"], what + " q_x")
+    gu.assert_equal(_f32_bits(g["s_x"]), _f32_bits(o["s_x"]), what + " s_x")
+    gu.assert_equal(g["acc"], o["acc"], what + " acc")
+    gu.assert_bf16_parity(g["y"], o["y"], what + " y")
+    gu.assert_bf16_parity(g["y2"], o["y"], what + " y (prepared codes)")
+
+
+def test_cfg1_tiny_all_stages(cr):
+    """Config 1 (64 x 512 x 256, 4 outlier channels x50) in full."""
+    d = workloads.make_linear(1)
+    g, o = run_all_stages(cr, d["x"], d["w"])
+    check_all(g, o, "cfg1")
+
+
+def test_cfg1_tiny_swiglu(cr):
+    """Config 1's weight read as a fused gate/up pair (i = 128)."""
+    d = workloads.make_linear(1)
+    g, o = run_all_stages(cr, d["x"], d["w"], swiglu=True)
+    check_all(g, o, "cfg1 swiglu")
+
+
+@pytest.mark.parametrize("m,n,k", [(1, 1, 256), (37, 100, 256), (300, 300, 768), (257, 513, 512),
+                                   (511, 130, 1024), (64, 256, 5376)])
+def test_ragged_shapes(cr, m, n, k):
+    """Ragged token and output counts: tails of partial 256-row tiles."""
+    rng = np.random.default_rng(m * 7 + n * 3 + k)
+    x = rng.standard_normal((m, k), dtype=np.float32)
+    x[:, rng.choice(k, 3, replace=False)] *= 40
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    g, o = run_all_stages(cr, workloads.to_bf16_bits(x), w)
+    check_all(g, o, "ragged %dx%dx%d" % (m, n, k))
+
+
+@pytest.mark.parametrize("m,i,k", [(5, 1, 256), (300, 100, 512), (130, 200, 768)])
+def test_ragged_swiglu(cr, m, i, k):
+    rng = np.random.default_rng(m + i + k)
+    x = rng.laplace(size=(m, k)).astype(np.float32)
+    w = (0.05 * rng.standard_normal((2 * i, k))).astype(np.float32)
+    g, o = run_all_stages(cr, workloads.to_bf16_bits(x), w, swiglu=True)
+    check_all(g, o, "swiglu ragged %dx%dx%d" % (m, i, k))
+
+
+def test_degenerate_rows(cr):
+    """All-zero rows (s = 0, codes 0, y = 0), rows of tiny values (the exact
+    division path for every element), a single non-zero, huge values."""
+    k, n = 512, 64
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((8, k), dtype=np.float32)
+    x[0] = 0
+    x[1] *= np.float32(1e-33)
+    x[2] = 0
+    x[2, 77] = 3.0
+    x[3] *= np.float32(1e30)
+    x[4, :256] = 0
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    w[0] = 0
+    w[1] *= np.float32(1e-35)
+    g, o = run_all_stages(cr, workloads.to_bf16_bits(x), w)
+    check_all(g, o, "degenerate")
+    assert g["s_x"][0] == 0 and not g["q_x"][0].any() and not g["y"][0].any()
+    assert g["s_w"][0] == 0 and not g["q_w"][0].any()
+
+
+def test_tie_rows_half_even(cr):
+    """Rows whose rotation is exactly a half-integer multiple of the scale
+    (amax 127 s) round half to even on the GPU as in the oracle."""
+    H = hd.H().astype(np.float64)
+    rng = np.random.default_rng(17)
+    values = [127.0, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5, -1.5, 126.5, -126.5, 4.5, -3.5, 0.0, 5.5, 6.5, -7.5]
+    rows = []
+    for e in (0, -3, 5, -10):
+        row = np.zeros(256 * len(values))
+        for gi, v in enumerate(values):
+            j = int(rng.integers(0, 256))
+            row[gi * 256:(gi + 1) * 256] = v * 2.0 ** e * H[:, j] / 16
+        rows.append(row)
+    x = np.array(rows)
+    assert hd.is_bf16_exact(x)
+    w = x.astype(np.float32)              # the same rows through the fp32 weight path
+    g, o = run_all_stages(cr, workloads.to_bf16_bits(x.astype(np.float32)), w)
+    check_all(g, o, "ties")
+
+
+def test_correctly_rounded_quotients(cr):
+    """Cases where rint(v * RN(1/s)) != rint(RN(v / s)) (exact rationals in the
+    oracle pins): the GPU takes the exact quotient."""
+    H = hd.H().astype(np.float64)
+    cases = [(56.25, -28.125), (61.0, 30.5), (44.75, 22.375), (9.8125, -4.90625),
+             (3.765625, -1.8828125), (43.75, 21.875), (19.5, 9.75), (19.5, -9.75)]
+    rows = []
+    for amax, v in cases:
+        row = np.zeros(512)
+        row[:256] = amax * H[:, 3] / 16
+        row[256:] = v * H[:, 77] / 16
+        rows.append(row)
+    x = np.array(rows).astype(np.float32)
+    rng = np.random.default_rng(3)
+    w = (0.1 * rng.standard_normal((32, 512))).astype(np.float32)
+    w[:8] = x                             # and the weight path
+    g, o = run_all_stages(cr, workloads.to_bf16_bits(x), w)
+    check_all(g, o, "quotients")
+
+
+def test_two_pass_long_rows(cr):
+    """k = 129 groups (33024) exceeds the register-resident row and takes the
+    recomputing second pass."""
+    rng = np.random.default_rng(9)
+    k = 129 * 256
+    x = rng.standard_normal((3, k), dtype=np.float32)
+    x[:, 5] *= 60
+    w = (0.01 * rng.standard_normal((40, k))).astype(np.float32)
+    g, o = run_all_stages(cr, workloads.to_bf16_bits(x), w)
+    check_all(g, o, "two-pass k=33024")
+
+
+def test_int32_extreme_at_max_k(cr):
+    """k = 133120, every code +-127: acc = +-127^2 k = +-2,147,092,480 exactly."""
+    import torch
+    k = 133120
+    qx = torch.full((3, k), 127, dtype=torch.int8, device="cuda")
+    qx[1] = -127
+    qw = torch.full((2, k), 127, dtype=torch.int8, device="cuda")
+    acc = gu.host(cr.gemm_s32(qx, qw))
+    assert acc[0, 0] == 2147092480 and acc[1, 1] == -2147092480 and acc[2, 0] == 2147092480
+
+
+def test_max_k_rotate_quant(cr):
+    """The largest k the boundary accepts, through rotation and quantization."""
+    rng = np.random.default_rng(10)
+    k = 133120
+    x = rng.standard_normal((2, k), dtype=np.float32)
+    xb = workloads.to_bf16_bits(x)
+    qx, sx = cr.rotate_quant_act(gu.dev_bf16(xb))
+    oq, os_ = oracle.rotate_quant_act(xb)
+    gu.assert_equal(gu.host(qx), oq, "q_x max k")
+    gu.assert_equal(_f32_bits(gu.host(sx)), _f32_bits(os_), "s_x max k")
+
+
+def test_zero_size_calls(cr):
+    import torch
+    x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    q, s = cr.rotate_quant_act(x)
+    assert q.shape == (0, 256) and s.shape == (0,)
+    qw = torch.zeros((4, 256), dtype=torch.int8, device="cuda")
+    sw = torch.zeros((4,), dtype=torch.float32, device="cuda")
+    y = cr.linear(x, qw, sw)
+    assert y.shape == (0, 4)
+
+
+def test_invalid_arguments_raise(cr):
+    import torch
+    x = torch.zeros((4, 300), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(cr.ConvRotError) as e:
+        cr.rotate_quant_act(x)
+    assert e.value.status == 2
+    x = torch.zeros((4, 512), dtype=torch.bfloat16, device="cuda")
+    qw = torch.zeros((8, 512), dtype=torch.int8, device="cuda")
+    sw = torch.zeros((8,), dtype=torch.float32, device="cuda")
+    ws = torch.zeros(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(cr.ConvRotError) as e:
+        cr.linear(x, qw, sw, workspace=ws)
+    assert e.value.status == 4
+
+
+def test_deterministic_and_row_chunking(cr):
+    """Same bytes on repeated calls, and splitting the tokens into chunks (the
+    caller's activation-memory knob) changes nothing: rows are independent."""
+    import torch
+    d = workloads.make_linear(2, m=700)
+    xd = gu.dev_bf16(d["x"])
+    qw, sw = cr.quantize_weight(gu.dev(d["w"][:1000]))
+    y1 = cr.linear(xd, qw, sw)
+    y2 = cr.linear(xd, qw, sw)
+    parts = [cr.linear(xd[a:b].contiguous(), qw, sw) for a, b in [(0, 1), (1, 300), (300, 700)]]
+    torch.cuda.synchronize()
+    assert torch.equal(y1.view(torch.int16), y2.view(torch.int16))
+    assert torch.equal(y1.view(torch.int16), torch.cat(parts).view(torch.int16))
