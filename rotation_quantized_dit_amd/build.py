@@ -21,7 +21,7 @@ SOURCES = ["convrot_api.cpp", "rotate_quant.hip", "gemm_i8.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
+    "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC",
     "-fhip-fp32-correctly-rounded-divide-sqrt", "-ffp-contract=off",
     "-fno-gpu-flush-denormals-to-zero", "-fno-fast-math",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -17,7 +17,7 @@
 // holds g and u of the same output element).  Each wave owns 128 x 128 as
 // 4 x 4 blocks of v_mfma_i32_32x32x32_i8 (32 x 32 outputs, 32 bytes of K per
 // instruction, 16 int32 accumulators per lane per block).  K advances 64
-// bytes per stage through a 3-stage LDS ring (32 KiB per stage).
+// bytes per stage through a 4-stage LDS ring (32 KiB per stage, 128 KiB).
 //
 // Operand streaming.  Both operands are K-contiguous rows (q_x is [M, K] and
 // q_w is [N, K]), which is the MFMA operand layout: a lane takes 16
@@ -46,7 +46,7 @@ namespace {
 constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
-constexpr int STAGES = 3;
+constexpr int STAGES = 4;
 constexpr int NTHREADS = 256;
 constexpr int A_STAGE = BM * BK;
 constexpr int B_STAGE = BN * BK;
@@ -55,6 +55,8 @@ constexpr int GROUP_M = 8;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
@@ -82,19 +84,18 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ uint16_t bf16_rne(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x0040u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+// fp32 -> bf16 bits, round to nearest even (NaN kept quiet); branch-free.
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+    const uint32_t u = __float_as_uint(f);
+    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+    const uint32_t q = (u >> 16) | 0x0040u;
+    return ((u & 0x7fffffffu) > 0x7f800000u) ? q : r;
 }
 
 // Fixed fp32 exponential (Cody-Waite reduction + degree-7 Taylor, fused
 // multiply-adds, exact 2^k scaling); the same algorithm the layer's
 // definition fixes, evaluated op for op.
-__device__ __forceinline__ float exp_cw(float x) {
-    if (x > 88.72f) return __builtin_inff();
-    if (x < -86.0f) return 0.0f;
+__device__ __forceinline__ float exp_cw_core(float x) {
     const float kf = __builtin_rintf(x * 0x1.715476p+0f);
     float r = __builtin_fmaf(-kf, 0x1.62e4p-1f, x);
     r = __builtin_fmaf(-kf, 0x1.7f7d1cp-20f, r);
@@ -107,6 +108,16 @@ __device__ __forceinline__ float exp_cw(float x) {
     p = __builtin_fmaf(p, r, 1.0f);
     p = __builtin_fmaf(p, r, 1.0f);
     return __builtin_ldexpf(p, (int)kf);
+}
+
+// Evaluated branch-free: out-of-range arguments are replaced by 0 for the
+// polynomial and the result is selected afterwards (bit-identical in range).
+__device__ __forceinline__ float exp_cw(float x) {
+    const bool hi = x > 88.72f;
+    const bool lo = x < -86.0f;
+    const float xin = (hi || lo) ? 0.0f : x;
+    const float v = exp_cw_core(xin);
+    return hi ? __builtin_inff() : (lo ? 0.0f : v);
 }
 
 __device__ __forceinline__ float dequant(int acc, float sx, float sw) {
@@ -139,52 +150,82 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * STAGE_BYTES];
 
     const int tid = threadIdx.x;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
     const int wm = wave >> 1;
     const int wn = wave & 1;
     const Tile tile = map_tile(blockIdx.x, MT, NT);
     const int m0 = tile.tm * BM;
 
-    // Source rows of this lane's four A and four B direct loads.  Load i of
-    // wave w fills LDS rows 16 * (4w + i) .. +15; lane l writes row l / 4 of
-    // that slab at chunk position l % 4, which holds logical chunk
-    // (l % 4) ^ swz(row).
-    const int8_t* a_src[4];
-    const int8_t* b_src[4];
+    // Epilogue scales, loaded before the main loop so their latency is hidden:
+    // s_x of the wave's 128 rows (two per lane) and s_w of the lane's 8
+    // output columns (gate and up columns for SwiGLU).
+    const int grow0 = m0 + (wave >> 1) * 128;
+    float sx_pre0 = 0.0f, sx_pre1 = 0.0f;
+    constexpr int EPI_CG = EP == Epilogue::SWIGLU ? 8 : 16;       // column groups per wave row
+    const int epi_cg = lane % EPI_CG;
+    const int epi_ro = lane / EPI_CG;
+    const int epi_col0 = EP == Epilogue::SWIGLU ? tile.tn * (BN / 2) + 64 * (wave & 1) + 8 * epi_cg
+                                                : tile.tn * BN + 128 * (wave & 1) + 8 * epi_cg;
+    float swa[8], swb[8];
+    if constexpr (EP != Epilogue::S32) {
+        const int ra = grow0 + lane, rb = grow0 + 64 + lane;
+        sx_pre0 = sx[ra < M ? ra : M - 1];
+        sx_pre1 = sx[rb < M ? rb : M - 1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = (epi_col0 + e) < N ? (epi_col0 + e) : (N - 1);
+            swa[e] = sw[c];
+            swb[e] = EP == Epilogue::SWIGLU ? sw[N + c] : 0.0f;
+        }
+    }
+
+    // Direct loads.  Load i of wave w fills LDS rows 16 * (4w + i) .. +15 of the
+    // A (and B) slab of a stage; lane l writes row l / 4 of that group at chunk
+    // position l % 4, which holds logical chunk (l % 4) ^ swz(row).  Addresses
+    // are a uniform tile base plus a per-lane 32-bit offset (< 256 * K).
+    const int8_t* a_base = A + (int64_t)m0 * K;
+    const int8_t* b_base;
+    int b_first;   // first weight row of this tile (gate rows for SwiGLU)
+    if constexpr (EP == Epilogue::SWIGLU)
+        b_first = tile.tn * (BN / 2);
+    else
+        b_first = tile.tn * BN;
+    b_base = B + (int64_t)b_first * K;
+    uint32_t a_voff[4], b_voff[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int rr = 16 * (4 * wave + i) + (lane >> 2);
         const int c = (lane & 3) ^ swz(rr);
         int am = m0 + rr;
         am = am < M ? am : M - 1;
-        a_src[i] = A + (int64_t)am * K + 16 * c;
+        a_voff[i] = (uint32_t)((am - m0) * K + 16 * c);
         int bn;
         if constexpr (EP == Epilogue::SWIGLU) {
-            const int n0 = tile.tn * (BN / 2);
-            int col = n0 + (rr & 127);
+            int col = b_first + (rr & 127);
             col = col < N ? col : N - 1;
-            bn = rr < 128 ? col : N + col;
+            bn = rr < 128 ? col : N + col;   // up rows live N rows further on
         } else {
-            bn = tile.tn * BN + rr;
+            bn = b_first + rr;
             bn = bn < N ? bn : N - 1;
         }
-        b_src[i] = B + (int64_t)bn * K + 16 * c;
+        b_voff[i] = (uint32_t)((int64_t)(bn - b_first) * K + 16 * c);
     }
 
     auto issue = [&](int kt, int slot) {
-        int8_t* a_dst = lds + slot * STAGE_BYTES + 1024 * (4 * wave);
+        int8_t* a_dst = lds + slot * STAGE_BYTES + 4096 * wave;
         int8_t* b_dst = a_dst + A_STAGE;
-        const int koff = kt * BK;
+        const int8_t* ak = a_base + kt * BK;
+        const int8_t* bk = b_base + kt * BK;
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds(a_src[i] + koff, (lds_void*)(a_dst + 1024 * i), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(ak + a_voff[i], (lds_void*)(a_dst + 1024 * i), 16, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds(b_src[i] + koff, (lds_void*)(b_dst + 1024 * i), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(bk + b_voff[i], (lds_void*)(b_dst + 1024 * i), 16, 0, 0);
     };
 
-    // LDS offsets of this lane's fragment rows (row part only).
+    // LDS rows of this lane's fragments.
     int a_row[4], b_row[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -203,88 +244,211 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
 
-    const int KT = K / BK;
+    // Byte offsets (within a stage) of this lane's 16-byte fragment reads for
+    // the two 32-byte k-steps of a stage.
+    int a_off[2][4], b_off[2][4];
 #pragma unroll
-    for (int st = 0; st < STAGES - 1; ++st)
-        if (st < KT) issue(st, st);
-
-    for (int kt = 0; kt < KT; ++kt) {
-        if (kt < KT - 1)
-            wait_vmcnt<8>();
-        else
-            wait_vmcnt<0>();
-        lds_barrier();
-        if (kt + STAGES - 1 < KT) issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-
-        const int8_t* As = lds + (kt % STAGES) * STAGE_BYTES;
-        const int8_t* Bs = As + A_STAGE;
+    for (int s = 0; s < 2; ++s) {
+        const int c = 2 * s + (lane >> 5);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) {
-            const int c = 2 * s + (lane >> 5);
-            v4i af[4], bf[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                af[i] = *reinterpret_cast<const v4i*>(As + a_row[i] * BK + 16 * (c ^ swz(a_row[i])));
-#pragma unroll
-            for (int j = 0; j < 4; ++j)
-                bf[j] = *reinterpret_cast<const v4i*>(Bs + b_row[j] * BK + 16 * (c ^ swz(b_row[j])));
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int j = 0; j < 4; ++j)
-                    acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+        for (int i = 0; i < 4; ++i) {
+            a_off[s][i] = a_row[i] * BK + 16 * (c ^ swz(a_row[i]));
+            b_off[s][i] = A_STAGE + b_row[i] * BK + 16 * (c ^ swz(b_row[i]));
         }
     }
+    auto read_frags = [&](const int8_t* st, int s, v4i (&af)[4], v4i (&bf)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            af[i] = *reinterpret_cast<const v4i*>(st + a_off[s][i]);
+            bf[i] = *reinterpret_cast<const v4i*>(st + b_off[s][i]);
+        }
+    };
+    auto mma = [&](const v4i (&af)[4], const v4i (&bf)[4]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+    };
 
-    // Epilogue.  Block (i, j) lane l register r holds acc row
-    // 32 i + 8 (r / 4) + 4 (l / 32) + r % 4 and column 32 j + l % 32 of the
-    // wave's 128 x 128 sub-tile.
-    const int col_lane = lane & 31;
-    const int row_lane = 4 * (lane >> 5);
+    // Software pipeline.  All STAGES slots are filled up front.  In stage kt:
+    //   k-step 0: MFMAs on registers set 0, interleaved with the reads of
+    //             k-step 1 into set 1;
+    //   barrier:  stage kt + 1 has landed (vmcnt) and every wave has read both
+    //             k-steps of stage kt (lgkmcnt before the barrier);
+    //   k-step 1: MFMAs on set 1, interleaved with the refill of stage kt's
+    //             slot with stage kt + STAGES and the reads of stage kt + 1's
+    //             k-step 0 into set 0.
+    // The steady-state loop runs while a refill remains (vmcnt: two later
+    // stages may stay in flight); the last stages are peeled so that the loop
+    // body is straight-line code.
+    const int KT = K / BK;
+#pragma unroll
+    for (int st = 0; st < STAGES; ++st)
+        if (st < KT) issue(st, st);
+    {
+        const int ahead = (KT - 1) < (STAGES - 1) ? (KT - 1) : (STAGES - 1);
+        if (ahead >= 3) wait_vmcnt<24>();
+        else if (ahead == 2) wait_vmcnt<16>();
+        else if (ahead == 1) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
+    }
+    lds_barrier();
+    v4i fa0[4], fb0[4], fa1[4], fb1[4];
+    read_frags(lds, 0, fa0, fb0);
+
+    int kt = 0;
+    for (; kt + STAGES < KT; ++kt) {
+        const int slot = kt & (STAGES - 1);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1);
+        mma(fa0, fb0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<16>();
+        lds_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(lds + ((kt + 1) & (STAGES - 1)) * STAGE_BYTES, 0, fa0, fb0);
+        issue(kt + STAGES, slot);
+        mma(fa1, fb1);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one direct load
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    // Peeled tail: at most STAGES - 1 stages with a successor, then the last.
+    for (; kt + 1 < KT; ++kt) {
+        const int slot = kt & (STAGES - 1);
+        read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1);
+        mma(fa0, fb0);
+        const int after = KT - 2 - kt;   // stages behind kt + 1 still in flight
+        if (after >= 2) wait_vmcnt<16>();
+        else if (after == 1) wait_vmcnt<8>();
+        else wait_vmcnt<0>();
+        lds_barrier();
+        read_frags(lds + ((kt + 1) & (STAGES - 1)) * STAGE_BYTES, 0, fa0, fb0);
+        mma(fa1, fb1);
+    }
+    read_frags(lds + (kt & (STAGES - 1)) * STAGE_BYTES, 1, fa1, fb1);
+    mma(fa0, fb0);
+    mma(fa1, fb1);
+
+    // Epilogue.  Block (i, j), lane l, register r of the MFMA accumulators
+    // holds row 32 i + 8 (r / 4) + 4 (l / 32) + r % 4 and column 32 j + l % 32
+    // of the wave's 128 x 128 sub-tile.  Row block by row block, each wave
+    // parks its 32 x 128 int32 accumulators in its own quarter of the (now
+    // free) LDS ring, then reads them back row-contiguous: every lane takes 8
+    // consecutive columns of one row, applies the scales (loaded once) and
+    // the epilogue math in a compact loop, and writes one 16-byte store.
+    lds_barrier();   // every wave is done reading the ring
+    int32_t* stash = reinterpret_cast<int32_t*>(lds + wave * (STAGES * STAGE_BYTES / 4));
+    constexpr int PITCH = 136;   // int32 per stashed row (bank-spread padding)
+    float* sxl = reinterpret_cast<float*>(stash + 32 * PITCH);   // the wave's 128 row scales
+    const bool full_tile_rows = m0 + BM <= M;
+    if constexpr (EP != Epilogue::S32) {
+        sxl[lane] = sx_pre0;
+        sxl[64 + lane] = sx_pre1;
+    }
+
+    auto stash_block = [&](int i) {
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                stash[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * PITCH + 32 * j + (lane & 31)] =
+                    acc[i][j][r];
+        asm volatile("" ::: "memory");
+    };
+
+    const int col0 = epi_col0;
+    const int cg = epi_cg;
+    const int ro = epi_ro;
+    const bool vec = full_tile_rows && (col0 + 8 <= N) && (N % 8 == 0);
     if constexpr (EP == Epilogue::SWIGLU) {
+        // lane -> 8 output columns (gate j, up i + j) and a row phase of 8
         uint16_t* y = reinterpret_cast<uint16_t*>(out);
-        const int n0 = tile.tn * (BN / 2) + 64 * wn;
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-            const int col = n0 + 32 * j + col_lane;
-            if (col >= N) continue;
-            const float swg = sw[col];
-            const float swu = sw[N + col];
+        for (int i = 0; i < 4; ++i) {
+            stash_block(i);
+#pragma nounroll
+            for (int it = 0; it < 4; ++it) {
+                const int lr = 8 * it + ro;
+                const int grow = grow0 + 32 * i + lr;
+                const float sxr = sxl[32 * i + lr];
+                const v4i g0 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg);
+                const v4i g1 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg + 4);
+                const v4i u0 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 64 + 8 * cg);
+                const v4i u1 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 64 + 8 * cg + 4);
+                const int ga[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+                const int ua[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+                uint32_t h[8];
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+                for (int e = 0; e < 8; ++e) {
+                    const float g = dequant(ga[e], sxr, swa[e]);
+                    const float u = dequant(ua[e], sxr, swb[e]);
+                    h[e] = bf16_rne((g / (1.0f + exp_cw(-g))) * u);
+                }
+                if (vec) {
+                    v4u pk = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                              h[6] | (h[7] << 16)};
+                    *reinterpret_cast<v4u*>(y + (int64_t)grow * N + col0) = pk;
+                } else if (grow < M) {
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + row_lane + (r & 3);
-                    if (row < M) {
-                        const float sxr = sx[row];
-                        const float g = dequant(acc[i][j][r], sxr, swg);
-                        const float u = dequant(acc[i][j + 2][r], sxr, swu);
-                        const float sl = g / (1.0f + exp_cw(-g));
-                        y[(int64_t)row * N + col] = bf16_rne(sl * u);
-                    }
+                    for (int e = 0; e < 8; ++e)
+                        if (col0 + e < N) y[(int64_t)grow * N + col0 + e] = (uint16_t)h[e];
                 }
             }
         }
     } else {
-        const int n0 = tile.tn * BN + wn * 128;
+        // lane -> 8 output columns and a row phase of 4
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            const int col = n0 + 32 * j + col_lane;
-            if (col >= N) continue;
-            float swc = 0.0f;
-            if constexpr (EP == Epilogue::BF16) swc = sw[col];
+        for (int i = 0; i < 4; ++i) {
+            stash_block(i);
+#pragma nounroll
+            for (int it = 0; it < 8; ++it) {
+                const int lr = 4 * it + ro;
+                const int grow = grow0 + 32 * i + lr;
+                const v4i a0 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg);
+                const v4i a1 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg + 4);
+                if constexpr (EP == Epilogue::S32) {
+                    int32_t* o = reinterpret_cast<int32_t*>(out);
+                    if (vec) {
+                        *reinterpret_cast<v4i*>(o + (int64_t)grow * N + col0) = a0;
+                        *reinterpret_cast<v4i*>(o + (int64_t)grow * N + col0 + 4) = a1;
+                    } else if (grow < M) {
+                        const int av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
+                        for (int e = 0; e < 8; ++e)
+                            if (col0 + e < N) o[(int64_t)grow * N + col0 + e] = av[e];
+                    }
+                } else {
+                    uint16_t* y = reinterpret_cast<uint16_t*>(out);
+                    const float sxr = sxl[32 * i + lr];
+                    const int av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+                    uint32_t h[8];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int row = m0 + wm * 128 + 32 * i + 8 * (r >> 2) + row_lane + (r & 3);
-                    if (row < M) {
-                        if constexpr (EP == Epilogue::S32) {
-                            reinterpret_cast<int32_t*>(out)[(int64_t)row * N + col] = acc[i][j][r];
-                        } else {
-                            reinterpret_cast<uint16_t*>(out)[(int64_t)row * N + col] =
-                                bf16_rne(dequant(acc[i][j][r], sx[row], swc));
-                        }
+                    for (int e = 0; e < 8; ++e) h[e] = bf16_rne(dequant(av[e], sxr, swa[e]));
+                    if (vec) {
+                        v4u pk = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                  h[6] | (h[7] << 16)};
+                        *reinterpret_cast<v4u*>(y + (int64_t)grow * N + col0) = pk;
+                    } else if (grow < M) {
+#pragma unroll
+                        for (int e = 0; e < 8; ++e)
+                            if (col0 + e < N) y[(int64_t)grow * N + col0 + e] = (uint16_t)h[e];
                     }
                 }
             }

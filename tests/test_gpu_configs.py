@@ -1,0 +1,206 @@
+"""GPU parity at the full workload sizes, in the launch configuration the
+benchmark times (full M per call).
+
+Configs 2-4: codes and scales of every weight row and every token row are
+compared bit for bit with the oracle; int32 accumulators and bf16 outputs on
+sampled rows (first, last, the ragged tail when present, 64 seeded random
+rows) that the oracle computes row by row.
+
+Config 5 (one block's linear chain, M = 32464 = 32256 video + 208 audio
+tokens): the GPU runs the whole chain on its own outputs; the oracle runs the
+same chain on its own outputs for the sampled rows (and, for the mixing step,
+the value rows they draw from).  Every stage is bit-exact by construction, so
+the two free-running chains must agree bit for bit at every layer.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def cr():
+    import rotation_quantized_dit_amd as cr
+    cr.load_library()
+    oracle.lib()
+    return cr
+
+
+def _f32_bits(a):
+    return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+
+
+def _run_linear_config(cr, cid):
+    import torch
+    c = workloads.CONFIGS[cid]
+    print("config %d: generating %s" % (cid, c.desc), flush=True)
+    d = workloads.make_linear(cid)
+    rows = workloads.sample_rows(c.m, seed=cid)
+    xd, wd = gu.dev_bf16(d["x"]), gu.dev(d["w"])
+    qw_d, sw_d = cr.quantize_weight(wd)
+    qx_d, sx_d = cr.rotate_quant_act(xd)
+    acc_d = cr.gemm_s32(qx_d, qw_d)
+    acc_rows = gu.host(acc_d[torch.from_numpy(rows).cuda()])
+    del acc_d
+    if c.swiglu:
+        y_d = cr.linear_swiglu(xd, qw_d, sw_d)
+        y2_d = cr.gemm_swiglu(qx_d, sx_d, qw_d, sw_d)
+    else:
+        y_d = cr.linear(xd, qw_d, sw_d)
+        y2_d = cr.gemm_dequant(qx_d, sx_d, qw_d, sw_d)
+    ridx = torch.from_numpy(rows).cuda()
+    g = dict(q_w=gu.host(qw_d), s_w=gu.host(sw_d), q_x=gu.host(qx_d), s_x=gu.host(sx_d),
+             acc=acc_rows, y=gu.host_bf16(y_d[ridx]), y2=gu.host_bf16(y2_d[ridx]))
+    del y_d, y2_d, qx_d, qw_d, xd, wd
+    torch.cuda.synchronize()
+    print("config %d: oracle" % cid, flush=True)
+    oqw, osw = oracle.quantize_weight(d["w"])
+    oqx, osx = oracle.rotate_quant_act(d["x"])
+    acc = oracle.gemm_s32(oqx[rows], oqw)
+    y = oracle.swiglu_bf16(acc, osx[rows], osw) if c.swiglu else oracle.dequant_bf16(acc, osx[rows], osw)
+    o = dict(q_w=oqw, s_w=osw, q_x=oqx, s_x=osx, acc=acc, y=y)
+    return g, o, rows
+
+
+@pytest.fixture(scope="module")
+def cfg2(cr):
+    return _run_linear_config(cr, 2)
+
+
+@pytest.fixture(scope="module")
+def cfg3(cr):
+    return _run_linear_config(cr, 3)
+
+
+@pytest.fixture(scope="module")
+def cfg4(cr):
+    return _run_linear_config(cr, 4)
+
+
+def _check_codes(run, what):
+    g, o, _ = run
+    gu.assert_equal(g["q_w"], o["q_w"], what + " q_w (all rows)")
+    gu.assert_equal(_f32_bits(g["s_w"]), _f32_bits(o["s_w"]), what + " s_w (all rows)")
+    gu.assert_equal(g["q_x"], o["q_x"], what + " q_x (all rows)")
+    gu.assert_equal(_f32_bits(g["s_x"]), _f32_bits(o["s_x"]), what + " s_x (all rows)")
+
+
+def _check_outputs(run, what):
+    g, o, rows = run
+    gu.assert_equal(g["acc"], o["acc"], what + " int32 acc (sampled rows)")
+    gu.assert_bf16_parity(g["y"], o["y"], what + " y (sampled rows)")
+    gu.assert_bf16_parity(g["y2"], o["y"], what + " y via prepared codes (sampled rows)")
+
+
+def test_cfg2_qkv_codes(cfg2):
+    _check_codes(cfg2, "cfg2")
+
+
+def test_cfg2_qkv_outputs(cfg2):
+    _check_outputs(cfg2, "cfg2")
+
+
+def test_cfg3_ffn_up_swiglu_codes(cfg3):
+    _check_codes(cfg3, "cfg3")
+
+
+def test_cfg3_ffn_up_swiglu_outputs(cfg3):
+    _check_outputs(cfg3, "cfg3")
+
+
+def test_cfg4_ffn_down_codes(cfg4):
+    _check_codes(cfg4, "cfg4")
+
+
+def test_cfg4_ffn_down_outputs(cfg4):
+    _check_outputs(cfg4, "cfg4")
+
+
+# ------------------------------------------------------------------ config 5
+
+
+def _oracle_chain(ch, rows, qws, sws):
+    """The block's linear chain for the given final rows, oracle only (torch CPU
+    for the synthetic mixing and outlier steps, which belong to the inputs)."""
+    import torch
+    x0 = torch.from_numpy(ch["x0"].view(np.int16)).view(torch.bfloat16)
+    p1, p2 = ch["perm"]
+    idx = ch["idx"]
+    x1 = workloads.chain_outliers(x0, idx[0])
+    need = np.unique(np.concatenate([rows, p1[rows], p2[rows]]))
+    x1_bits = x1.view(torch.int16).numpy().view(np.uint16)
+    qkv = oracle.linear_rows(x1_bits, qws[0], sws[0], need)            # full QKV rows
+    pos = {r: i for i, r in enumerate(need)}
+    v = torch.from_numpy(qkv[:, workloads.V_COLS[0]:workloads.V_COLS[1]].copy().view(np.int16)).view(torch.bfloat16)
+    a = workloads.chain_mix(v[[pos[r] for r in p1[rows]]], v[[pos[r] for r in p2[rows]]])
+    x2 = workloads.chain_outliers(a, idx[1]).view(torch.int16).numpy().view(np.uint16)
+    o2 = oracle.linear_rows(x2, qws[1], sws[1])
+    x3 = workloads.chain_outliers(torch.from_numpy(o2.view(np.int16)).view(torch.bfloat16), idx[2])
+    o3 = oracle.linear_swiglu_rows(x3.view(torch.int16).numpy().view(np.uint16), qws[2], sws[2])
+    x4 = workloads.chain_outliers(torch.from_numpy(o3.view(np.int16)).view(torch.bfloat16), idx[3])
+    o4 = oracle.linear_rows(x4.view(torch.int16).numpy().view(np.uint16), qws[3], sws[3])
+    return {"qkv": qkv[[pos[r] for r in rows]], "attn_out": o2, "ffn_up": o3, "ffn_down": o4}
+
+
+@pytest.fixture(scope="module")
+def cfg5(cr):
+    import torch
+    print("config 5: generating the block chain inputs", flush=True)
+    ch = workloads.make_chain()
+    m = ch["m"]
+    rows = workloads.sample_rows(m, seed=5, count=48)
+    p1, p2 = (torch.from_numpy(p).cuda() for p in ch["perm"])
+    idx = ch["idx"]
+    gq, gs = [], []
+    for w in ch["w"]:
+        q, s = cr.quantize_weight(gu.dev(w))
+        gq.append(q)
+        gs.append(s)
+    x0 = gu.dev_bf16(ch["x0"])
+    x1 = workloads.chain_outliers(x0, idx[0])
+    qkv = cr.linear(x1, gq[0], gs[0])
+    v = qkv[:, workloads.V_COLS[0]:workloads.V_COLS[1]]
+    a = workloads.chain_mix(v[p1], v[p2]).contiguous()
+    x2 = workloads.chain_outliers(a, idx[1])
+    o2 = cr.linear(x2, gq[1], gs[1])
+    x3 = workloads.chain_outliers(o2, idx[2])
+    o3 = cr.linear_swiglu(x3, gq[2], gs[2])
+    x4 = workloads.chain_outliers(o3, idx[3])
+    o4 = cr.linear(x4, gq[3], gs[3])
+    ridx = torch.from_numpy(rows).cuda()
+    g = {"qkv": gu.host_bf16(qkv[ridx]), "attn_out": gu.host_bf16(o2[ridx]),
+         "ffn_up": gu.host_bf16(o3[ridx]), "ffn_down": gu.host_bf16(o4[ridx]),
+         "q_w": [gu.host(q) for q in gq], "s_w": [gu.host(s) for s in gs],
+         "finite": bool(torch.isfinite(o4.float()).all().item())}
+    del qkv, v, a, x2, o2, x3, o3, x4, o4, gq, gs
+    torch.cuda.synchronize()
+    print("config 5: oracle", flush=True)
+    qws, sws = zip(*[oracle.quantize_weight(w) for w in ch["w"]])
+    o = _oracle_chain(ch, rows, qws, sws)
+    o["q_w"], o["s_w"] = list(qws), list(sws)
+    return g, o, rows
+
+
+def test_cfg5_weights_all_rows(cfg5):
+    g, o, _ = cfg5
+    for layer in range(4):
+        gu.assert_equal(g["q_w"][layer], o["q_w"][layer], "cfg5 layer %d q_w" % layer)
+        gu.assert_equal(_f32_bits(g["s_w"][layer]), _f32_bits(o["s_w"][layer]), "cfg5 layer %d s_w" % layer)
+
+
+@pytest.mark.parametrize("layer", ["qkv", "attn_out", "ffn_up", "ffn_down"])
+def test_cfg5_chain_layer(cfg5, layer):
+    g, o, rows = cfg5
+    gu.assert_bf16_parity(g[layer], o[layer], "cfg5 %s (sampled rows incl. the audio tail)" % layer)
+
+
+def test_cfg5_chain_finite_and_tail_rows(cfg5):
+    """No NaN/Inf anywhere in the final output, and the 208-row audio tail above
+    32256 (a partial 256-row tile) is among the checked rows."""
+    g, _, rows = cfg5
+    assert g["finite"]
+    assert np.any(rows >= workloads.VIDEO_TOKENS) and rows.max() == 32463
