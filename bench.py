@@ -4,7 +4,7 @@ One step is one pass of the whole hot path over one batch: the FFN of one
 MiniMax H3 DiT block at 32256 tokens (hidden 5376, FFN width 14336):
     x [32256, 5376] bf16 --rotate+quant--> codes --int8 GEMM + SwiGLU--> h [32256, 14336] bf16
     h --rotate+quant--> codes --int8 GEMM + dequant--> y [32256, 5376] bf16
-(the FFN-up configuration with its Laplace activations, chained into the
+(the FFN-up workload with its Laplace activations, chained into the
 FFN-down weights).  Weights are rotated and quantized once, before timing
 (load-time; they stay quantized in memory); that step is timed separately.
 
@@ -38,17 +38,39 @@ def log(msg):
 
 
 def make_down_weight():
-    """W_down [5376, 14336] exactly as the FFN-down config draws it."""
+    """W_down [5376, 14336] exactly as the FFN-down workload draws it."""
     import workloads
-    c4 = workloads.CONFIGS[4]
+    c4 = workloads.WORKLOADS["ffn_down"]
     rng = np.random.default_rng(c4.seed)
-    # skip the two activation draws of that config without materialising them
+    # skip the two activation draws of that workload without materialising them
     for _ in range(2):
         for r0 in range(0, c4.m, 4096):
             rng.standard_normal((min(4096, c4.m - r0), c4.k), dtype=np.float32)
     w = rng.standard_normal((c4.n, c4.k), dtype=np.float32)
     w *= np.float32(0.01)
     return w
+
+
+def measured_traffic(kernel):
+    """HBM-side bytes per launch of a GEMM kernel from the committed counter
+    profile (profiles/gemm_ffn_traffic.txt), scaled by the copy calibration;
+    None when the GEMM source has changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "gemm_ffn_traffic.txt")
+    src = os.path.join(ROOT, "rotation_quantized_dit_amd", "csrc", "gemm_i8.hip")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if "=" in line and not line.lstrip().startswith("#"):
+            key, val = line.split("=", 1)
+            kv[key.strip()] = val.strip()
+    if kv.get("gemm_source_sha256") != hashlib.sha256(open(src, "rb").read()).hexdigest():
+        return None
+    cb = float(kv["copy_bytes"])
+    fetch = float(kv[kernel + ".fetch_kib"]) * cb / float(kv["copy_fetch_kib"])
+    write = float(kv[kernel + ".write_kib"]) * cb / float(kv["copy_write_kib"])
+    return fetch + write
 
 
 def cpu_baseline(x_bits, w_up, w_dn, target_s=12.0):
@@ -70,7 +92,7 @@ def cpu_baseline(x_bits, w_up, w_dn, target_s=12.0):
 
     r = 4
     t = run(r)
-    rows = max(4, min(512, int(r * target_s / max(t, 1e-3))))
+    rows = max(4, min(4096, int(r * target_s / max(t, 1e-3))))
     log("cpu baseline: %d rows (probe %d rows took %.2f s)" % (rows, r, t))
     t = run(rows)
     ops = 2.0 * rows * (n_up * k_up + n_dn * k_dn)
@@ -88,8 +110,8 @@ def main():
     ap.add_argument("--m", type=int, default=None, help="token rows (default 32256)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build runs the layer on a single MI355X "
-              "(token sharding across GPUs needs no exchange and is not launched here)",
+        print("bench.py measures one GPU only: the layer runs on a single MI355X here "
+              "(token sharding across GPUs needs no exchange and is not launched)",
               file=sys.stderr)
         sys.exit(2)
 
@@ -102,7 +124,7 @@ def main():
     log("generating inputs")
     t0 = time.perf_counter()
     import workloads
-    up = workloads.make_linear(3, m=args.m)
+    up = workloads.make_linear("ffn_up", m=args.m)
     x_bits, w_up = up["x"], up["w"]
     w_dn = make_down_weight()
     log("inputs ready in %.1f s" % (time.perf_counter() - t0))
@@ -217,8 +239,9 @@ def main():
     roofline = {"kernel": "gemm_swiglu_up (int8 MFMA GEMM + SwiGLU epilogue)", "bound": "mfma",
                 "achieved": round(ops_up / (d_up * 1e-3) / 1e12, 1), "peak": PEAK_INT8_TOPS,
                 "unit": "TOP/s", "frac": round(ops_up / (d_up * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
-                "traffic": None,
-                "per_launch_ops": ops_up}
+                "traffic": measured_traffic("gemm_swiglu_up"),
+                "per_launch_ops": ops_up,
+                "per_launch_min_bytes": M * K1 + N1 * K1 + 2 * M * I + 4 * (M + N1)}
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -256,8 +256,9 @@ void orc_dequant_bf16(const int32_t* acc, int64_t nrows, int64_t n, const float*
 
 /* Fixed fp32 exponential used by silu.
  *
- * The pages do not say how the SwiGLU epilogue evaluates exp; this build fixes
- * one algorithm so that the fused epilogue is reproducible bit for bit:
+ * The pages do not say how the SwiGLU epilogue evaluates exp; the layer's
+ * definition here fixes one algorithm so that the fused epilogue is
+ * reproducible bit for bit:
  *   Cody and Waite argument reduction (W. J. Cody, W. Waite, "Software Manual
  *   for the Elementary Functions", 1980): k = rint(x * log2(e)),
  *   r = x - k*ln2 with ln2 split into a 15-bit head (so k*head is exact) and

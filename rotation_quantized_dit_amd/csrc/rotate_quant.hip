@@ -91,30 +91,32 @@ __device__ __forceinline__ void butterfly16(float v[16]) {
     }
 }
 
-struct Smem {
-    float tr[kMaxWaves][4][16][17];     // per-wave 16 x 16 transposes, padded
-    uint8_t codes[kMaxWaves][4][256];   // per-wave code staging
-    float red[kMaxWaves];
-};
+// LDS per wave: four 16 x 17 fp32 transpose tiles, one per 256-element
+// group the wave holds at a time (the 17th column pads the banks: tiles sit
+// 272 words apart, i.e. 16 banks apart modulo 64).  The same memory later
+// stages that wave's int8 codes.  Transposes are private to one wave, and a
+// wave executes its LDS instructions in order, so they need no workgroup
+// barrier, only a compiler fence.
+constexpr int kTile = 16 * 17;
+constexpr int kWaveFloats = 4 * kTile;
 
-template <typename Tin>
-__device__ __forceinline__ void rotate_group(const Tin* __restrict__ xr, int g, bool ok, int wave,
-                                             int sub, int j, Smem& sm, float out[16]) {
-    float v[16];
-    if (ok) {
-        load16(xr + (int64_t)g * 256 + j * 16, v);
-    } else {
+__device__ __forceinline__ void wave_fence() {
+    __builtin_amdgcn_wave_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Phase 2 of the butterfly for the 16 values of one lane-slot, after phase 1
+// ran on its contiguous block: transpose through the slot's tile, then spans
+// 16..128.  Returns the rotated (unnormalized) values of elements
+// j, 16 + j, ..., 240 + j.
+__device__ __forceinline__ void transpose_phase2(float* tile, int j, float v[16]) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) v[i] = 0.0f;
-    }
+    for (int i = 0; i < 16; ++i) tile[j * 17 + i] = v[i];
+    wave_fence();
+#pragma unroll
+    for (int b = 0; b < 16; ++b) v[b] = tile[b * 17 + j];
+    wave_fence();
     butterfly16(v);
-#pragma unroll
-    for (int i = 0; i < 16; ++i) sm.tr[wave][sub][j][i] = v[i];
-    __syncthreads();
-#pragma unroll
-    for (int b = 0; b < 16; ++b) out[b] = sm.tr[wave][sub][b][j];
-    __syncthreads();
-    butterfly16(out);
 }
 
 __device__ __forceinline__ int quant_one(float v_un, float r16, float s, bool exact_all) {
@@ -127,12 +129,35 @@ __device__ __forceinline__ int quant_one(float v_un, float r16, float s, bool ex
     return (int)n;
 }
 
-// P = groups per lane-slot held in registers (two-pass when TWO_PASS).
-template <typename Tin, int P, bool TWO_PASS>
-__global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_kernel(
-    const Tin* __restrict__ x, int64_t k, int passes, int8_t* __restrict__ q,
-    float* __restrict__ s_out) {
-    __shared__ Smem sm;
+// Quantize one slot's 16 rotated values (elements j + 16 b) and store the
+// group's 256 codes in natural order: bytes are staged in the slot's tile and
+// read back as one 16-byte chunk per lane (elements 16 j .. 16 j + 15).
+__device__ __forceinline__ void quant_store(float* tile, int j, const float t[16], float r16,
+                                            float s, bool zero, bool exact_all, bool ok,
+                                            int8_t* __restrict__ dst) {
+    uint8_t* cb = reinterpret_cast<uint8_t*>(tile);
+#pragma unroll
+    for (int b = 0; b < 16; ++b) {
+        const int c = zero ? 0 : quant_one(t[b], r16, s, exact_all);
+        cb[b * 16 + j] = (uint8_t)(int8_t)c;
+    }
+    wave_fence();
+    if (ok) {
+        const v4u c16 = *reinterpret_cast<const v4u*>(cb + j * 16);
+        *reinterpret_cast<v4u*>(dst + j * 16) = c16;
+    }
+    wave_fence();
+}
+
+// One workgroup per row; W = blockDim / 64 waves hold 4 groups each per pass
+// and P passes of the row in registers; all of a lane's loads are issued
+// before any transform.  The row maximum goes through LDS (one workgroup
+// barrier per row).
+template <typename Tin, int P>
+__global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_rows_kernel(
+    const Tin* __restrict__ x, int64_t k, int8_t* __restrict__ q, float* __restrict__ s_out) {
+    extern __shared__ float smem[];
+    __shared__ float red[kMaxWaves];
     const int64_t row = blockIdx.x;
     const int G = (int)(k >> 8);
     const int W = blockDim.x >> 6;
@@ -141,64 +166,106 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_kernel(
     const int sub = lane >> 4;
     const int j = lane & 15;
     const Tin* xr = x + row * k;
+    int8_t* qr = q + row * k;
+    float* tile = smem + wave * kWaveFloats + sub * kTile;
 
     float vals[P][16];
-    float amax = 0.0f;
-    const int npass = TWO_PASS ? passes : P;
-    for (int p = 0; p < npass; ++p) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
         const int g = (p * W + wave) * 4 + sub;
-        const bool ok = g < G;
-        float t[16];
-        rotate_group(xr, g, ok, wave, sub, j, sm, t);
+        if (g < G) {
+            load16(xr + (int64_t)g * 256 + j * 16, vals[p]);
+        } else {
 #pragma unroll
-        for (int b = 0; b < 16; ++b) amax = __builtin_fmaxf(amax, __builtin_fabsf(t[b]));
-        if (!TWO_PASS) {
-#pragma unroll
-            for (int pp = 0; pp < P; ++pp)
-                if (pp == p) {
-#pragma unroll
-                    for (int b = 0; b < 16; ++b) vals[pp][b] = t[b];
-                }
+            for (int i = 0; i < 16; ++i) vals[p][i] = 0.0f;
         }
+    }
+    float amax = 0.0f;
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        butterfly16(vals[p]);
+        transpose_phase2(tile, j, vals[p]);
+#pragma unroll
+        for (int b = 0; b < 16; ++b) amax = __builtin_fmaxf(amax, __builtin_fabsf(vals[p][b]));
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off, 64));
-    if (lane == 0) sm.red[wave] = amax;
+    if (lane == 0) red[wave] = amax;
     __syncthreads();
-    amax = sm.red[0];
-    for (int w = 1; w < W; ++w) amax = __builtin_fmaxf(amax, sm.red[w]);
+    amax = red[0];
+    for (int w = 1; w < W; ++w) amax = __builtin_fmaxf(amax, red[w]);
 
     const float s = (amax * 0.0625f) / 127.0f;
     if (threadIdx.x == 0) s_out[row] = s;
     const bool zero = !(s > 0.0f);
     const bool exact_all = !(s >= 0x1p-100f);
     const float r16 = zero ? 0.0f : (1.0f / s) * 0.0625f;
-
-    for (int p = 0; p < npass; ++p) {
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
         const int g = (p * W + wave) * 4 + sub;
-        const bool ok = g < G;
+        quant_store(tile, j, vals[p], r16, s, zero, exact_all, g < G, qr + (int64_t)g * 256);
+    }
+}
+
+// Rows longer than 32 W groups: one workgroup per row, the rotation is
+// computed twice (once for the row maximum, once to quantize) rather than
+// held in registers.
+template <typename Tin>
+__global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_long_kernel(
+    const Tin* __restrict__ x, int64_t k, int passes, int8_t* __restrict__ q,
+    float* __restrict__ s_out) {
+    extern __shared__ float smem[];
+    __shared__ float red[kMaxWaves];
+    const int64_t row = blockIdx.x;
+    const int G = (int)(k >> 8);
+    const int W = blockDim.x >> 6;
+    const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
+    const int sub = lane >> 4;
+    const int j = lane & 15;
+    const Tin* xr = x + row * k;
+    int8_t* qr = q + row * k;
+    float* tile = smem + wave * kWaveFloats + sub * kTile;
+
+    float amax = 0.0f;
+    for (int p = 0; p < passes; ++p) {
+        const int g = (p * W + wave) * 4 + sub;
         float t[16];
-        if (TWO_PASS) {
-            rotate_group(xr, g, ok, wave, sub, j, sm, t);
+        if (g < G) {
+            load16(xr + (int64_t)g * 256 + j * 16, t);
         } else {
 #pragma unroll
-            for (int pp = 0; pp < P; ++pp)
-                if (pp == p) {
+            for (int i = 0; i < 16; ++i) t[i] = 0.0f;
+        }
+        butterfly16(t);
+        transpose_phase2(tile, j, t);
 #pragma unroll
-                    for (int b = 0; b < 16; ++b) t[b] = vals[pp][b];
-                }
-        }
+        for (int b = 0; b < 16; ++b) amax = __builtin_fmaxf(amax, __builtin_fabsf(t[b]));
+    }
 #pragma unroll
-        for (int b = 0; b < 16; ++b) {
-            int c = zero ? 0 : quant_one(t[b], r16, s, exact_all);
-            sm.codes[wave][sub][b * 16 + j] = (uint8_t)(int8_t)c;
+    for (int off = 32; off > 0; off >>= 1) amax = __builtin_fmaxf(amax, __shfl_xor(amax, off, 64));
+    if (lane == 0) red[wave] = amax;
+    __syncthreads();
+    amax = red[0];
+    for (int w = 1; w < W; ++w) amax = __builtin_fmaxf(amax, red[w]);
+
+    const float s = (amax * 0.0625f) / 127.0f;
+    if (threadIdx.x == 0) s_out[row] = s;
+    const bool zero = !(s > 0.0f);
+    const bool exact_all = !(s >= 0x1p-100f);
+    const float r16 = zero ? 0.0f : (1.0f / s) * 0.0625f;
+    for (int p = 0; p < passes; ++p) {
+        const int g = (p * W + wave) * 4 + sub;
+        float t[16];
+        if (g < G) {
+            load16(xr + (int64_t)g * 256 + j * 16, t);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) t[i] = 0.0f;
         }
-        __syncthreads();
-        if (ok) {
-            uint4 c16 = *reinterpret_cast<const uint4*>(&sm.codes[wave][sub][j * 16]);
-            *reinterpret_cast<uint4*>(q + row * k + (int64_t)g * 256 + j * 16) = c16;
-        }
-        __syncthreads();
+        butterfly16(t);
+        transpose_phase2(tile, j, t);
+        quant_store(tile, j, t, r16, s, zero, exact_all, g < G, qr + (int64_t)g * 256);
     }
 }
 
@@ -206,20 +273,23 @@ template <typename Tin>
 hipError_t launch(const Tin* x, int64_t rows, int64_t k, int8_t* q, float* s, hipStream_t stream) {
     const int G = (int)(k / 256);
     // Prefer the fewest register-resident groups per slot, then the fewest waves.
-    int P = (G + 4 * kMaxWaves - 1) / (4 * kMaxWaves);
-    dim3 grid((unsigned)rows);
+    const int P = (G + 4 * kMaxWaves - 1) / (4 * kMaxWaves);
     if (P <= kMaxPasses) {
-        int W = (G + 4 * P - 1) / (4 * P);
+        const int W = (G + 4 * P - 1) / (4 * P);
         dim3 block(64 * W);
+        const size_t lds = (size_t)W * kWaveFloats * sizeof(float);
+        dim3 grid((unsigned)rows);
         switch (P) {
-            case 1: rotate_quant_kernel<Tin, 1, false><<<grid, block, 0, stream>>>(x, k, 1, q, s); break;
-            case 2: rotate_quant_kernel<Tin, 2, false><<<grid, block, 0, stream>>>(x, k, 2, q, s); break;
-            case 3: rotate_quant_kernel<Tin, 3, false><<<grid, block, 0, stream>>>(x, k, 3, q, s); break;
-            default: rotate_quant_kernel<Tin, 4, false><<<grid, block, 0, stream>>>(x, k, 4, q, s); break;
+            case 1: rotate_quant_rows_kernel<Tin, 1><<<grid, block, lds, stream>>>(x, k, q, s); break;
+            case 2: rotate_quant_rows_kernel<Tin, 2><<<grid, block, lds, stream>>>(x, k, q, s); break;
+            case 3: rotate_quant_rows_kernel<Tin, 3><<<grid, block, lds, stream>>>(x, k, q, s); break;
+            default: rotate_quant_rows_kernel<Tin, 4><<<grid, block, lds, stream>>>(x, k, q, s); break;
         }
     } else {
+        dim3 grid((unsigned)rows);
         dim3 block(64 * kMaxWaves);
-        rotate_quant_kernel<Tin, 1, true><<<grid, block, 0, stream>>>(x, k, P, q, s);
+        const size_t lds = (size_t)kMaxWaves * kWaveFloats * sizeof(float);
+        rotate_quant_long_kernel<Tin><<<grid, block, lds, stream>>>(x, k, P, q, s);
     }
     return hipGetLastError();
 }

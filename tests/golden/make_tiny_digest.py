@@ -1,11 +1,11 @@
-"""Write tests/golden/cfg1_oracle_digest.txt: SHA-256 digests of the CPU
-oracle's results on the tiny config (64 x 512 x 256, seed 0).
+"""Write tests/golden/tiny_oracle_digest.txt: SHA-256 digests of the CPU
+oracle's results on the tiny workload (64 x 512 x 256, seed 0).
 
 It calls only the oracle and the seeded input generator.  The digests lock the
 oracle's arithmetic: any later change to it must come with a new digest and a
 commit message naming the passage (or the reading of it) that justifies it.
 
-Run from the repository root:  python tests/golden/make_cfg1_digest.py
+Run from the repository root:  python tests/golden/make_tiny_digest.py
 """
 import hashlib
 import os
@@ -19,7 +19,7 @@ import workloads  # noqa: E402
 
 
 def digests():
-    d = workloads.make_linear(1)
+    d = workloads.make_linear("tiny")
     qw, sw = oracle.quantize_weight(d["w"])
     qx, sx = oracle.rotate_quant_act(d["x"])
     acc = oracle.gemm_s32(qx, qw)
@@ -33,9 +33,9 @@ def digests():
 
 
 if __name__ == "__main__":
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "cfg1_oracle_digest.txt")
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "tiny_oracle_digest.txt")
     with open(path, "w") as f:
-        f.write("# SHA-256 of the oracle's arrays on the tiny config (written by make_cfg1_digest.py)\n")
+        f.write("# SHA-256 of the oracle's arrays on the tiny workload (written by make_tiny_digest.py)\n")
         for k, v in digests().items():
             f.write("%s %s\n" % (k, v))
     print(open(path).read())

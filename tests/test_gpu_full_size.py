@@ -1,16 +1,18 @@
 """GPU parity at the full workload sizes, in the launch configuration the
 benchmark times (full M per call).
 
-Configs 2-4: codes and scales of every weight row and every token row are
-compared bit for bit with the oracle; int32 accumulators and bf16 outputs on
-sampled rows (first, last, the ragged tail when present, 64 seeded random
-rows) that the oracle computes row by row.
+QKV (4096 x 5376 x 16128), FFN up + SwiGLU (32256 x 5376 x 2 x 14336) and FFN
+down (32256 x 14336 x 5376): codes and scales of every weight row and every
+token row are compared bit for bit with the oracle; int32 accumulators and
+bf16 outputs on sampled rows (first, last, 64 seeded random rows) that the
+oracle computes row by row.
 
-Config 5 (one block's linear chain, M = 32464 = 32256 video + 208 audio
-tokens): the GPU runs the whole chain on its own outputs; the oracle runs the
-same chain on its own outputs for the sampled rows (and, for the mixing step,
-the value rows they draw from).  Every stage is bit-exact by construction, so
-the two free-running chains must agree bit for bit at every layer.
+One block's linear chain (M = 32464 = 32256 video + 208 audio tokens): the
+GPU runs the whole chain on its own outputs; the oracle runs the same chain on
+its own outputs for the sampled rows (and, for the mixing step, the value rows
+they draw from).  Every stage is bit-exact by construction, so the two
+free-running chains must agree bit for bit at every layer, including the rows
+of the ragged 208-row audio tail.
 """
 import numpy as np
 import pytest
@@ -34,12 +36,12 @@ def _f32_bits(a):
     return np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
 
 
-def _run_linear_config(cr, cid):
+def _run_linear_workload(cr, name):
     import torch
-    c = workloads.CONFIGS[cid]
-    print("config %d: generating %s" % (cid, c.desc), flush=True)
-    d = workloads.make_linear(cid)
-    rows = workloads.sample_rows(c.m, seed=cid)
+    c = workloads.WORKLOADS[name]
+    print("%s: generating %s" % (name, c.desc), flush=True)
+    d = workloads.make_linear(name)
+    rows = workloads.sample_rows(c.m, seed=c.seed)
     xd, wd = gu.dev_bf16(d["x"]), gu.dev(d["w"])
     qw_d, sw_d = cr.quantize_weight(wd)
     qx_d, sx_d = cr.rotate_quant_act(xd)
@@ -57,7 +59,7 @@ def _run_linear_config(cr, cid):
              acc=acc_rows, y=gu.host_bf16(y_d[ridx]), y2=gu.host_bf16(y2_d[ridx]))
     del y_d, y2_d, qx_d, qw_d, xd, wd
     torch.cuda.synchronize()
-    print("config %d: oracle" % cid, flush=True)
+    print("%s: oracle" % name, flush=True)
     oqw, osw = oracle.quantize_weight(d["w"])
     oqx, osx = oracle.rotate_quant_act(d["x"])
     acc = oracle.gemm_s32(oqx[rows], oqw)
@@ -67,18 +69,18 @@ def _run_linear_config(cr, cid):
 
 
 @pytest.fixture(scope="module")
-def cfg2(cr):
-    return _run_linear_config(cr, 2)
+def qkv(cr):
+    return _run_linear_workload(cr, "qkv")
 
 
 @pytest.fixture(scope="module")
-def cfg3(cr):
-    return _run_linear_config(cr, 3)
+def ffn_up(cr):
+    return _run_linear_workload(cr, "ffn_up")
 
 
 @pytest.fixture(scope="module")
-def cfg4(cr):
-    return _run_linear_config(cr, 4)
+def ffn_down(cr):
+    return _run_linear_workload(cr, "ffn_down")
 
 
 def _check_codes(run, what):
@@ -96,31 +98,31 @@ def _check_outputs(run, what):
     gu.assert_bf16_parity(g["y2"], o["y"], what + " y via prepared codes (sampled rows)")
 
 
-def test_cfg2_qkv_codes(cfg2):
-    _check_codes(cfg2, "cfg2")
+def test_qkv_codes(qkv):
+    _check_codes(qkv, "qkv")
 
 
-def test_cfg2_qkv_outputs(cfg2):
-    _check_outputs(cfg2, "cfg2")
+def test_qkv_outputs(qkv):
+    _check_outputs(qkv, "qkv")
 
 
-def test_cfg3_ffn_up_swiglu_codes(cfg3):
-    _check_codes(cfg3, "cfg3")
+def test_ffn_up_swiglu_codes(ffn_up):
+    _check_codes(ffn_up, "ffn_up")
 
 
-def test_cfg3_ffn_up_swiglu_outputs(cfg3):
-    _check_outputs(cfg3, "cfg3")
+def test_ffn_up_swiglu_outputs(ffn_up):
+    _check_outputs(ffn_up, "ffn_up")
 
 
-def test_cfg4_ffn_down_codes(cfg4):
-    _check_codes(cfg4, "cfg4")
+def test_ffn_down_codes(ffn_down):
+    _check_codes(ffn_down, "ffn_down")
 
 
-def test_cfg4_ffn_down_outputs(cfg4):
-    _check_outputs(cfg4, "cfg4")
+def test_ffn_down_outputs(ffn_down):
+    _check_outputs(ffn_down, "ffn_down")
 
 
-# ------------------------------------------------------------------ config 5
+# ------------------------------------------------------------------ block chain
 
 
 def _oracle_chain(ch, rows, qws, sws):
@@ -147,12 +149,12 @@ def _oracle_chain(ch, rows, qws, sws):
 
 
 @pytest.fixture(scope="module")
-def cfg5(cr):
+def block_chain(cr):
     import torch
-    print("config 5: generating the block chain inputs", flush=True)
+    print("block chain: generating the inputs", flush=True)
     ch = workloads.make_chain()
     m = ch["m"]
-    rows = workloads.sample_rows(m, seed=5, count=48)
+    rows = workloads.sample_rows(m, seed=workloads.WORKLOADS["block_chain"].seed, count=48)
     p1, p2 = (torch.from_numpy(p).cuda() for p in ch["perm"])
     idx = ch["idx"]
     gq, gs = [], []
@@ -178,29 +180,29 @@ def cfg5(cr):
          "finite": bool(torch.isfinite(o4.float()).all().item())}
     del qkv, v, a, x2, o2, x3, o3, x4, o4, gq, gs
     torch.cuda.synchronize()
-    print("config 5: oracle", flush=True)
+    print("block chain: oracle", flush=True)
     qws, sws = zip(*[oracle.quantize_weight(w) for w in ch["w"]])
     o = _oracle_chain(ch, rows, qws, sws)
     o["q_w"], o["s_w"] = list(qws), list(sws)
     return g, o, rows
 
 
-def test_cfg5_weights_all_rows(cfg5):
-    g, o, _ = cfg5
+def test_block_chain_weights_all_rows(block_chain):
+    g, o, _ = block_chain
     for layer in range(4):
-        gu.assert_equal(g["q_w"][layer], o["q_w"][layer], "cfg5 layer %d q_w" % layer)
-        gu.assert_equal(_f32_bits(g["s_w"][layer]), _f32_bits(o["s_w"][layer]), "cfg5 layer %d s_w" % layer)
+        gu.assert_equal(g["q_w"][layer], o["q_w"][layer], "chain layer %d q_w" % layer)
+        gu.assert_equal(_f32_bits(g["s_w"][layer]), _f32_bits(o["s_w"][layer]), "chain layer %d s_w" % layer)
 
 
 @pytest.mark.parametrize("layer", ["qkv", "attn_out", "ffn_up", "ffn_down"])
-def test_cfg5_chain_layer(cfg5, layer):
-    g, o, rows = cfg5
-    gu.assert_bf16_parity(g[layer], o[layer], "cfg5 %s (sampled rows incl. the audio tail)" % layer)
+def test_block_chain_layer(block_chain, layer):
+    g, o, rows = block_chain
+    gu.assert_bf16_parity(g[layer], o[layer], "chain %s (sampled rows incl. the audio tail)" % layer)
 
 
-def test_cfg5_chain_finite_and_tail_rows(cfg5):
+def test_block_chain_finite_and_tail_rows(block_chain):
     """No NaN/Inf anywhere in the final output, and the 208-row audio tail above
     32256 (a partial 256-row tile) is among the checked rows."""
-    g, _, rows = cfg5
+    g, _, rows = block_chain
     assert g["finite"]
     assert np.any(rows >= workloads.VIDEO_TOKENS) and rows.max() == 32463

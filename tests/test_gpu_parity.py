@@ -59,18 +59,18 @@ def check_all(g, o, what):
     gu.assert_bf16_parity(g["y2"], o["y"], what + " y (prepared codes)")
 
 
-def test_cfg1_tiny_all_stages(cr):
-    """Config 1 (64 x 512 x 256, 4 outlier channels x50) in full."""
-    d = workloads.make_linear(1)
+def test_tiny_all_stages(cr):
+    """The tiny workload (64 x 512 x 256, 4 outlier channels x50) in full."""
+    d = workloads.make_linear("tiny")
     g, o = run_all_stages(cr, d["x"], d["w"])
-    check_all(g, o, "cfg1")
+    check_all(g, o, "tiny")
 
 
-def test_cfg1_tiny_swiglu(cr):
-    """Config 1's weight read as a fused gate/up pair (i = 128)."""
-    d = workloads.make_linear(1)
+def test_tiny_swiglu(cr):
+    """The tiny workload's weight read as a fused gate/up pair (i = 128)."""
+    d = workloads.make_linear("tiny")
     g, o = run_all_stages(cr, d["x"], d["w"], swiglu=True)
-    check_all(g, o, "cfg1 swiglu")
+    check_all(g, o, "tiny swiglu")
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 256), (37, 100, 256), (300, 300, 768), (257, 513, 512),
@@ -220,7 +220,7 @@ def test_deterministic_and_row_chunking(cr):
     """Same bytes on repeated calls, and splitting the tokens into chunks (the
     caller's activation-memory knob) changes nothing: rows are independent."""
     import torch
-    d = workloads.make_linear(2, m=700)
+    d = workloads.make_linear("qkv", m=700)
     xd = gu.dev_bf16(d["x"])
     qw, sw = cr.quantize_weight(gu.dev(d["w"][:1000]))
     y1 = cr.linear(xd, qw, sw)

@@ -120,8 +120,8 @@ def test_rotation_is_groupwise_and_contiguous():
 
 def test_rotation_invariance_of_the_product():
     """(x H)(W H)^T = x W^T: the oracle's fp32 rotation of both operands keeps the
-    fp64 product within the propagated butterfly bound, on all of config 1 (C6)."""
-    d = workloads.make_linear(1)
+    fp64 product within the propagated butterfly bound, on all of the tiny workload (C6)."""
+    d = workloads.make_linear("tiny")
     x = hd.bf16_bits_to_f64(d["x"])
     w = d["w"].astype(np.float64)
     xr = oracle.rotate_rows(x.astype(np.float32)).astype(np.float64)
@@ -172,7 +172,7 @@ def test_quantizer_invariants():
     v[9] = np.float32(2.0) ** rng.integers(-60, 60, 512)
     q, s = oracle.quantize_rows(v)
     _check_quant_invariants(v, q, s)
-    d = workloads.make_linear(1)
+    d = workloads.make_linear("tiny")
     qx, sx = oracle.rotate_quant_act(d["x"])
     xr = oracle.rotate_rows(oracle.bf16_to_f32(d["x"]))
     _check_quant_invariants(xr, qx, sx)
@@ -393,12 +393,12 @@ def _rel_fro(y_bits, exact):
     return np.linalg.norm(y - exact) / np.linalg.norm(exact)
 
 
-@pytest.mark.parametrize("cid,rows", [(1, None), (2, 48)])
-def test_rotation_beats_unrotated_int8(cid, rows):
+@pytest.mark.parametrize("name,rows", [("tiny", None), ("qkv", 48)])
+def test_rotation_beats_unrotated_int8(name, rows):
     """The method's claim (RESEARCH.md, "Weight families"): on inputs with
     outlier channels the rotated int8 product is far closer to x W^T than
     per-token int8 without rotation (same oracle with H replaced by I) (C12)."""
-    d = workloads.make_linear(cid, m=rows)
+    d = workloads.make_linear(name, m=rows)
     x = hd.bf16_bits_to_f64(d["x"])
     exact = x @ d["w"].astype(np.float64).T
     qw, sw = oracle.quantize_weight(d["w"])
@@ -413,7 +413,7 @@ def test_rotation_beats_unrotated_int8(cid, rows):
 
 def test_determinism_across_thread_counts():
     """Rows are independent, so results are identical for 1 and many threads (C13)."""
-    d = workloads.make_linear(1)
+    d = workloads.make_linear("tiny")
     before = oracle.get_threads()
     try:
         oracle.set_threads(1)
@@ -429,7 +429,7 @@ def test_determinism_across_thread_counts():
 def test_row_subset_equals_full():
     """Processing a subset of rows gives exactly those rows of the full result
     (what the full-size parity tests rely on)."""
-    d = workloads.make_linear(1)
+    d = workloads.make_linear("tiny")
     qw, sw = oracle.quantize_weight(d["w"])
     full = oracle.linear_rows(d["x"], qw, sw)
     rows = np.array([63, 0, 17, 17, 40])
@@ -532,11 +532,11 @@ def test_golden_closed_forms():
         assert np.all(got[np.arange(256) % 4 == int(i)] == float(val))
 
 
-def test_cfg1_digest_unchanged():
-    """The oracle's tiny-config results match the committed digests (a lock
+def test_tiny_digest_unchanged():
+    """The oracle's tiny-workload results match the committed digests (a lock
     against unintended changes of its arithmetic or of the input generator)."""
-    from tests.golden.make_cfg1_digest import digests
+    from tests.golden.make_tiny_digest import digests
     import os
-    path = os.path.join(os.path.dirname(__file__), "golden", "cfg1_oracle_digest.txt")
+    path = os.path.join(os.path.dirname(__file__), "golden", "tiny_oracle_digest.txt")
     want = dict(l.split() for l in open(path) if l.strip() and not l.startswith("#"))
     assert digests() == want

@@ -16,7 +16,7 @@ choices (the pages do not state them).  Outlier channels stand in for the
 activation outliers that the rotation spreads (RESEARCH.md, "Weight
 families"); their count and magnitude are synthetic.
 
-Draw order per config is fixed below; numpy ``default_rng(seed)`` (PCG64).
+Draw order per workload is fixed below; numpy ``default_rng(seed)`` (PCG64).
 """
 from __future__ import annotations
 
@@ -32,8 +32,7 @@ AUDIO_TOKENS = 208
 
 
 @dataclass(frozen=True)
-class Config:
-    cid: int
+class Workload:
     name: str
     m: int
     k: int
@@ -43,17 +42,17 @@ class Config:
     desc: str
 
 
-CONFIGS = {
-    1: Config(1, "tiny", 64, 512, 256, False, 0,
-              "tiny ConvRot linear 64x512x256, 4 outlier channels x50"),
-    2: Config(2, "qkv", 4096, HIDDEN, QKV, False, 1,
-              "fused QKV projection 4096x5376x16128, 1% outlier channels x30"),
-    3: Config(3, "ffn_up_swiglu", VIDEO_TOKENS, HIDDEN, 2 * FFN, True, 2,
-              "FFN up + fused SwiGLU 32256x5376x(2x14336), Laplace(0,1) activations"),
-    4: Config(4, "ffn_down", VIDEO_TOKENS, FFN, HIDDEN, False, 3,
-              "FFN down 32256x14336x5376, SwiGLU-like activations"),
-    5: Config(5, "block_chain", VIDEO_TOKENS + AUDIO_TOKENS, HIDDEN, 0, False, 4,
-              "one block's linear chain, M=32464: QKV, attn-out, FFN up+SwiGLU, FFN down"),
+WORKLOADS = {
+    "tiny": Workload("tiny", 64, 512, 256, False, 0,
+                     "tiny ConvRot linear 64x512x256, 4 outlier channels x50"),
+    "qkv": Workload("qkv", 4096, HIDDEN, QKV, False, 1,
+                    "fused QKV projection 4096x5376x16128, 1% outlier channels x30"),
+    "ffn_up": Workload("ffn_up", VIDEO_TOKENS, HIDDEN, 2 * FFN, True, 2,
+                       "FFN up + fused SwiGLU 32256x5376x(2x14336), Laplace(0,1) activations"),
+    "ffn_down": Workload("ffn_down", VIDEO_TOKENS, FFN, HIDDEN, False, 3,
+                         "FFN down 32256x14336x5376, SwiGLU-like activations"),
+    "block_chain": Workload("block_chain", VIDEO_TOKENS + AUDIO_TOKENS, HIDDEN, 0, False, 4,
+                            "one block's linear chain, M=32464: QKV, attn-out, FFN up+SwiGLU, FFN down"),
 }
 
 
@@ -71,29 +70,30 @@ def _normal(rng, shape, std=1.0):
     return x
 
 
-def make_linear(cid: int, m: int | None = None) -> dict:
-    """Inputs for configs 1-4: ``x`` raw bf16 [m, k] (uint16), ``w`` fp32 [n, k].
+def make_linear(name: str, m: int | None = None) -> dict:
+    """Inputs of a single-linear workload: ``x`` raw bf16 [m, k] (uint16),
+    ``w`` fp32 [n, k].
 
-    ``m`` < the config's M keeps the first m token rows of the same draw
+    ``m`` < the workload's M keeps the first m token rows of the same draw
     (rows are drawn first-to-last, so a prefix is a prefix); the full weight
     is always drawn."""
-    c = CONFIGS[cid]
-    assert not (cid == 5)
+    c = WORKLOADS[name]
+    assert name != "block_chain"
     rng = np.random.default_rng(c.seed)
-    if cid == 1:
+    if name == "tiny":
         idx = rng.choice(c.k, 4, replace=False)
         x = _normal(rng, (c.m, c.k))
         x[:, idx] *= np.float32(50.0)
         w = _normal(rng, (c.n, c.k), 0.02)
-    elif cid == 2:
+    elif name == "qkv":
         idx = rng.choice(c.k, 54, replace=False)
         x = _normal(rng, (c.m, c.k))
         x[:, idx] *= np.float32(30.0)
         w = _normal(rng, (c.n, c.k), 0.02)
-    elif cid == 3:
+    elif name == "ffn_up":
         x = rng.laplace(0.0, 1.0, (c.m, c.k)).astype(np.float32)
         w = _normal(rng, (c.n, c.k), 0.02)
-    elif cid == 4:
+    elif name == "ffn_down":
         import torch
         a = torch.from_numpy(_normal(rng, (c.m, c.k)))
         b = torch.from_numpy(_normal(rng, (c.m, c.k)))
@@ -101,13 +101,13 @@ def make_linear(cid: int, m: int | None = None) -> dict:
         del a, b
         w = _normal(rng, (c.n, c.k), 0.01)
     else:
-        raise ValueError(cid)
+        raise ValueError(name)
     if m is not None:
         x = x[:m]
-    return {"x": to_bf16_bits(x), "w": w, "cfg": c}
+    return {"x": to_bf16_bits(x), "w": w, "workload": c}
 
 
-# ------------------------------------------------------------------ config 5
+# ------------------------------------------------------------------ block chain
 
 CHAIN_LAYERS = (
     # name, K, N (GEMM), swiglu, weight std
@@ -121,13 +121,13 @@ V_COLS = (2 * HIDDEN, 3 * HIDDEN)
 
 
 def make_chain(m: int | None = None) -> dict:
-    """Config 5 inputs: x0 raw bf16 [M, 5376] (before its outlier scaling), the
+    """Block-chain inputs: x0 raw bf16 [M, 5376] (before its outlier scaling), the
     four fp32 weights, four outlier channel sets and two row permutations.
 
     Draw order: x0, W_qkv, W_o, W_up, W_down, idx_1..idx_4, perm_1, perm_2.
     ``m`` < 32464 keeps a prefix of x0 and draws the permutations over m rows
     (a smaller but complete chain)."""
-    c = CONFIGS[5]
+    c = WORKLOADS["block_chain"]
     rng = np.random.default_rng(c.seed)
     x0 = _normal(rng, (c.m, HIDDEN))
     ws = [_normal(rng, (n, k), std) for (_, k, n, _, std) in CHAIN_LAYERS]
