@@ -90,9 +90,10 @@ def cpu_baseline(x_bits, w_up, w_dn, target_s=12.0):
         oracle.linear_rows(h, qwd, swd)
         return time.perf_counter() - t0
 
-    r = 4
+    # the oracle spreads rows over its threads: probe with a few rows per thread
+    r = 4 * threads
     t = run(r)
-    rows = max(4, min(4096, int(r * target_s / max(t, 1e-3))))
+    rows = max(r, min(8192, int(r * target_s / max(t, 1e-3))))
     log("cpu baseline: %d rows (probe %d rows took %.2f s)" % (rows, r, t))
     t = run(rows)
     ops = 2.0 * rows * (n_up * k_up + n_dn * k_dn)

@@ -12,21 +12,31 @@
 //            [0, i) are the gate, [i, 2i) the up projection);
 //            y[m][j] = bf16_rne(silu(g) * u), silu(g) = g / (1 + exp(-g)).
 //
-// Tiling.  A workgroup of 4 waves owns a 256 x 256 tile of acc (for SwiGLU:
-// 256 tokens x 128 gate columns + the matching 128 up columns, so every lane
-// holds g and u of the same output element).  Each wave owns 128 x 128 as
-// 4 x 4 blocks of v_mfma_i32_32x32x32_i8 (32 x 32 outputs, 32 bytes of K per
-// instruction, 16 int32 accumulators per lane per block).  K advances 64
-// bytes per stage through a 4-stage LDS ring (32 KiB per stage, 128 KiB).
+// Tiling.  A workgroup of 8 waves (two per SIMD) owns a 256 x 256 tile of acc
+// (for SwiGLU: 256 tokens x 128 gate columns + the matching 128 up columns).
+// Waves form a 4 (rows) x 2 (columns) grid; each owns 64 x 128 as 2 x 4
+// blocks of v_mfma_i32_32x32x32_i8 (32 x 32 outputs, 32 bytes of K per
+// instruction, 16 int32 accumulators per lane per block, 128 per lane in
+// all).  For SwiGLU a wave's 128 columns are 64 gate columns and the 64 up
+// columns of the same outputs, so every lane holds g and u of its elements.
+// K advances 64 bytes per stage through a 4-stage LDS ring (32 KiB per stage).
+//
+// Why two waves per SIMD: each SIMD issues at most one instruction per wave
+// every few cycles, and the fragment reads, the ring refills and their
+// address set-up of one wave would otherwise sit in the gaps of that same
+// wave's MFMA stream; with a second wave on the SIMD the matrix core takes
+// MFMAs from whichever wave has one ready.
 //
 // Operand streaming.  Both operands are K-contiguous rows (q_x is [M, K] and
 // q_w is [N, K]), which is the MFMA operand layout: a lane takes 16
-// contiguous bytes of one row.  Global -> LDS copies use the gfx950 direct
-// load (global_load_lds_dwordx4: 64 lanes x 16 B land contiguously in LDS, no
-// VGPR staging).  Each LDS row is 64 bytes (4 chunks of 16 B); chunk c of row r
-// is stored at position c ^ ((r >> 2) & 3), which makes the 16-byte fragment
-// reads of 16 consecutive rows hit distinct banks.  The XOR is applied on the
-// global address side, so the DMA writes stay contiguous.
+// contiguous bytes of one row.  Global -> LDS copies use the direct buffer
+// load (buffer_load_dwordx4 ... lds: 64 lanes x 16 B land contiguously in
+// LDS, no VGPR staging); the per-lane row offset is a fixed register, the
+// K position a scalar offset, so one copy costs one M0 move and one load.
+// Each LDS row is 64 bytes (4 chunks of 16 B); chunk c of row r is stored at
+// position c ^ ((r >> 2) & 3), which makes the 16-byte fragment reads of 16
+// consecutive rows hit distinct banks.  The XOR is applied on the global
+// side, so the copies stay contiguous in LDS.
 //
 // Scheduling.  Workgroups are dealt round-robin to the 8 XCDs; the tile id is
 // remapped so that each XCD walks a contiguous range of tiles in a grouped
@@ -47,15 +57,23 @@ constexpr int BM = 256;
 constexpr int BN = 256;
 constexpr int BK = 64;
 constexpr int STAGES = 4;
-constexpr int NTHREADS = 256;
+constexpr int NWAVES = 8;
+constexpr int NTHREADS = 64 * NWAVES;
 constexpr int A_STAGE = BM * BK;
 constexpr int B_STAGE = BN * BK;
 constexpr int STAGE_BYTES = A_STAGE + B_STAGE;
+constexpr int RING_BYTES = STAGES * STAGE_BYTES;
 constexpr int GROUP_M = 8;
+// Epilogue staging: each wave parks 32 rows x 128 int32 at a time, rows
+// padded to PITCH int32 to spread banks; it reuses the ring's memory.
+constexpr int PITCH = 136;
+constexpr int STASH_WAVE_BYTES = 32 * PITCH * 4;
+constexpr int LDS_BYTES = RING_BYTES > NWAVES * STASH_WAVE_BYTES ? RING_BYTES : NWAVES * STASH_WAVE_BYTES;
+// copies per wave per stage: A rows [32 w, 32 w + 32) and B rows [32 w, 32 w + 32)
+constexpr int COPIES = 4;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
-typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -69,12 +87,12 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-// Workgroup barrier for the LDS ring.  Completion of the direct global->LDS
-// copies is established by the explicit vmcnt wait that precedes it, and the
-// fragment reads of the previous stage by an lgkmcnt(0) wait; so only the
-// hardware barrier is needed, plus a compiler barrier that keeps LDS accesses
-// on their side of it.  (A fenced __syncthreads() would drain every
-// outstanding prefetch with vmcnt(0).)
+// Workgroup barrier for the LDS ring.  Completion of the direct copies is
+// established by the explicit vmcnt wait that precedes it, and the fragment
+// reads of the previous stage by an lgkmcnt(0) wait; so only the hardware
+// barrier is needed, plus a compiler barrier that keeps LDS accesses on their
+// side of it.  (A fenced __syncthreads() would drain every outstanding
+// prefetch with vmcnt(0).)
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
     // lgkmcnt(0): this wave's fragment reads are complete before any wave can
@@ -82,6 +100,20 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
+}
+
+// One direct copy: 64 lanes x 16 bytes from rsrc + voff + soff into LDS at
+// dst + 16 * lane.
+__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t rsrc, int8_t* dst, uint32_t voff,
+                                       uint32_t soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voff, soff, 0, 0);
+#endif
+}
+
+// Buffer resource over [base, base + bytes) (raw, no stride; gfx9 dword 3).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const int8_t* base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
 }
 
 // fp32 -> bf16 bits, round to nearest even (NaN kept quiet); branch-free.
@@ -147,31 +179,29 @@ template <Epilogue EP>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ B,
     const float* __restrict__ sw, int M, int N, int K, void* __restrict__ out, int MT, int NT) {
-    __shared__ __attribute__((aligned(1024))) int8_t lds[STAGES * STAGE_BYTES];
+    __shared__ __attribute__((aligned(1024))) int8_t lds[LDS_BYTES];
+    __shared__ float sx_lds[BM];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
+    const int wm = wave >> 1;   // 64-row band of the tile
+    const int wn = wave & 1;    // column half of the tile
     const Tile tile = map_tile(blockIdx.x, MT, NT);
     const int m0 = tile.tm * BM;
+    const int rows_a = (M - m0) < BM ? (M - m0) : BM;
 
     // Epilogue scales, loaded before the main loop so their latency is hidden:
-    // s_x of the wave's 128 rows (two per lane) and s_w of the lane's 8
-    // output columns (gate and up columns for SwiGLU).
-    const int grow0 = m0 + (wave >> 1) * 128;
-    float sx_pre0 = 0.0f, sx_pre1 = 0.0f;
-    constexpr int EPI_CG = EP == Epilogue::SWIGLU ? 8 : 16;       // column groups per wave row
+    // s_x of the tile's 256 rows (into LDS, read back per output row) and s_w
+    // of the lane's 8 output columns (gate and up columns for SwiGLU).
+    constexpr int EPI_CG = EP == Epilogue::SWIGLU ? 8 : 16;   // column groups per wave row
     const int epi_cg = lane % EPI_CG;
     const int epi_ro = lane / EPI_CG;
-    const int epi_col0 = EP == Epilogue::SWIGLU ? tile.tn * (BN / 2) + 64 * (wave & 1) + 8 * epi_cg
-                                                : tile.tn * BN + 128 * (wave & 1) + 8 * epi_cg;
+    const int epi_col0 = EP == Epilogue::SWIGLU ? tile.tn * (BN / 2) + 64 * wn + 8 * epi_cg
+                                                : tile.tn * BN + 128 * wn + 8 * epi_cg;
     float swa[8], swb[8];
     if constexpr (EP != Epilogue::S32) {
-        const int ra = grow0 + lane, rb = grow0 + 64 + lane;
-        sx_pre0 = sx[ra < M ? ra : M - 1];
-        sx_pre1 = sx[rb < M ? rb : M - 1];
+        if (tid < BM) sx_lds[tid] = sx[tid < rows_a ? m0 + tid : M - 1];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int c = (epi_col0 + e) < N ? (epi_col0 + e) : (N - 1);
@@ -180,95 +210,97 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         }
     }
 
-    // Direct loads.  Load i of wave w fills LDS rows 16 * (4w + i) .. +15 of the
-    // A (and B) slab of a stage; lane l writes row l / 4 of that group at chunk
-    // position l % 4, which holds logical chunk (l % 4) ^ swz(row).  Addresses
-    // are a uniform tile base plus a per-lane 32-bit offset (< 256 * K).
-    const int8_t* a_base = A + (int64_t)m0 * K;
-    const int8_t* b_base;
+    // Copy sources.  Copy i of wave w fills LDS rows 32 w + 16 i .. +15 of the
+    // A slab (i = 0, 1) or of the B slab (i = 2, 3) of a stage; lane l writes
+    // row (l / 4) of that group at chunk position l % 4, which holds logical
+    // chunk (l % 4) ^ swz(row).  Offsets are relative to a per-panel buffer
+    // resource (the tile's A rows; its gate rows; its up rows).
     int b_first;   // first weight row of this tile (gate rows for SwiGLU)
     if constexpr (EP == Epilogue::SWIGLU)
         b_first = tile.tn * (BN / 2);
     else
         b_first = tile.tn * BN;
-    b_base = B + (int64_t)b_first * K;
-    uint32_t a_voff[4], b_voff[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int rr = 16 * (4 * wave + i) + (lane >> 2);
-        const int c = (lane & 3) ^ swz(rr);
-        int am = m0 + rr;
-        am = am < M ? am : M - 1;
-        a_voff[i] = (uint32_t)((am - m0) * K + 16 * c);
-        int bn;
-        if constexpr (EP == Epilogue::SWIGLU) {
-            int col = b_first + (rr & 127);
-            col = col < N ? col : N - 1;
-            bn = rr < 128 ? col : N + col;   // up rows live N rows further on
-        } else {
-            bn = b_first + rr;
-            bn = bn < N ? bn : N - 1;
-        }
-        b_voff[i] = (uint32_t)((int64_t)(bn - b_first) * K + 16 * c);
+    const int b_span = EP == Epilogue::SWIGLU ? BN / 2 : BN;
+    const int rows_b = (N - b_first) < b_span ? (N - b_first) : b_span;
+    const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(A + (int64_t)m0 * K, (uint32_t)rows_a * (uint32_t)K);
+    __amdgpu_buffer_rsrc_t rsrc_b;
+    if constexpr (EP == Epilogue::SWIGLU) {
+        // waves 0-3 copy B rows 0-127 (gate), waves 4-7 rows 128-255 (up)
+        const int64_t first = wave < 4 ? b_first : (int64_t)N + b_first;
+        rsrc_b = make_rsrc(B + first * K, (uint32_t)rows_b * (uint32_t)K);
+    } else {
+        rsrc_b = make_rsrc(B + (int64_t)b_first * K, (uint32_t)rows_b * (uint32_t)K);
     }
-
+    uint32_t voff[COPIES];
+#pragma unroll
+    for (int i = 0; i < COPIES; ++i) {
+        const int rr = 32 * wave + 16 * (i & 1) + (lane >> 2);   // row within the slab
+        const int c = (lane & 3) ^ swz(rr);
+        int src_row;
+        if (i < 2) {
+            src_row = rr < rows_a ? rr : rows_a - 1;
+        } else if constexpr (EP == Epilogue::SWIGLU) {
+            const int j = rr & 127;   // the gate or up row of output column b_first + j
+            src_row = j < rows_b ? j : rows_b - 1;
+        } else {
+            src_row = rr < rows_b ? rr : rows_b - 1;
+        }
+        voff[i] = (uint32_t)src_row * (uint32_t)K + 16u * (uint32_t)c;
+    }
     auto issue = [&](int kt, int slot) {
-        int8_t* a_dst = lds + slot * STAGE_BYTES + 4096 * wave;
+        int8_t* a_dst = lds + slot * STAGE_BYTES + 32 * 64 * wave;
         int8_t* b_dst = a_dst + A_STAGE;
-        const int8_t* ak = a_base + kt * BK;
-        const int8_t* bk = b_base + kt * BK;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds(ak + a_voff[i], (lds_void*)(a_dst + 1024 * i), 16, 0, 0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds(bk + b_voff[i], (lds_void*)(b_dst + 1024 * i), 16, 0, 0);
+        const uint32_t soff = (uint32_t)kt * BK;
+        copy16(rsrc_a, a_dst, voff[0], soff);
+        copy16(rsrc_a, a_dst + 1024, voff[1], soff);
+        copy16(rsrc_b, b_dst, voff[2], soff);
+        copy16(rsrc_b, b_dst + 1024, voff[3], soff);
     };
 
-    // LDS rows of this lane's fragments.
-    int a_row[4], b_row[4];
+    // LDS rows of this lane's fragments: A blocks a = 0, 1 (rows of the
+    // wave's band), B blocks b = 0..3 (for SwiGLU: b = 0, 1 gate, 2, 3 up).
+    int a_row[2], b_row[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        a_row[i] = wm * 128 + 32 * i + (lane & 31);
+    for (int a = 0; a < 2; ++a) a_row[a] = 64 * wm + 32 * a + (lane & 31);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
         if constexpr (EP == Epilogue::SWIGLU)
-            b_row[i] = (i < 2 ? 0 : 128) + 64 * wn + 32 * (i & 1) + (lane & 31);
+            b_row[b] = (b < 2 ? 0 : 128) + 64 * wn + 32 * (b & 1) + (lane & 31);
         else
-            b_row[i] = wn * 128 + 32 * i + (lane & 31);
+            b_row[b] = 128 * wn + 32 * b + (lane & 31);
     }
 
-    v16i acc[4][4];
+    v16i acc[2][4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int a = 0; a < 2; ++a)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0;
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
 
     // Byte offsets (within a stage) of this lane's 16-byte fragment reads for
     // the two 32-byte k-steps of a stage.
-    int a_off[2][4], b_off[2][4];
+    int a_off[2][2], b_off[2][4];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         const int c = 2 * s + (lane >> 5);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            a_off[s][i] = a_row[i] * BK + 16 * (c ^ swz(a_row[i]));
-            b_off[s][i] = A_STAGE + b_row[i] * BK + 16 * (c ^ swz(b_row[i]));
-        }
+        for (int a = 0; a < 2; ++a) a_off[s][a] = a_row[a] * BK + 16 * (c ^ swz(a_row[a]));
+#pragma unroll
+        for (int b = 0; b < 4; ++b) b_off[s][b] = A_STAGE + b_row[b] * BK + 16 * (c ^ swz(b_row[b]));
     }
-    auto read_frags = [&](const int8_t* st, int s, v4i (&af)[4], v4i (&bf)[4]) {
+    auto read_frags = [&](const int8_t* st, int s, v4i (&af)[2], v4i (&bf)[4]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            af[i] = *reinterpret_cast<const v4i*>(st + a_off[s][i]);
-            bf[i] = *reinterpret_cast<const v4i*>(st + b_off[s][i]);
-        }
+        for (int a = 0; a < 2; ++a) af[a] = *reinterpret_cast<const v4i*>(st + a_off[s][a]);
+#pragma unroll
+        for (int b = 0; b < 4; ++b) bf[b] = *reinterpret_cast<const v4i*>(st + b_off[s][b]);
     };
-    auto mma = [&](const v4i (&af)[4], const v4i (&bf)[4]) {
+    auto mma = [&](const v4i (&af)[2], const v4i (&bf)[4]) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+        for (int a = 0; a < 2; ++a)
 #pragma unroll
-            for (int j = 0; j < 4; ++j)
-                acc[i][j] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[i], bf[j], acc[i][j], 0, 0, 0);
+            for (int b = 0; b < 4; ++b)
+                acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], acc[a][b], 0, 0, 0);
     };
 
     // Software pipeline.  All STAGES slots are filled up front.  In stage kt:
@@ -280,21 +312,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     //             slot with stage kt + STAGES and the reads of stage kt + 1's
     //             k-step 0 into set 0.
     // The steady-state loop runs while a refill remains (vmcnt: two later
-    // stages may stay in flight); the last stages are peeled so that the loop
-    // body is straight-line code.
+    // stages, COPIES copies each, may stay in flight); the last stages are
+    // peeled so that the loop body is straight-line code.
     const int KT = K / BK;
 #pragma unroll
     for (int st = 0; st < STAGES; ++st)
         if (st < KT) issue(st, st);
     {
         const int ahead = (KT - 1) < (STAGES - 1) ? (KT - 1) : (STAGES - 1);
-        if (ahead >= 3) wait_vmcnt<24>();
-        else if (ahead == 2) wait_vmcnt<16>();
-        else if (ahead == 1) wait_vmcnt<8>();
+        if (ahead >= 3) wait_vmcnt<3 * COPIES>();
+        else if (ahead == 2) wait_vmcnt<2 * COPIES>();
+        else if (ahead == 1) wait_vmcnt<COPIES>();
         else wait_vmcnt<0>();
     }
     lds_barrier();
-    v4i fa0[4], fb0[4], fa1[4], fb1[4];
+    v4i fa0[2], fb0[4], fa1[2], fb1[4];
     read_frags(lds, 0, fa0, fb0);
 
     int kt = 0;
@@ -304,28 +336,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1);
         mma(fa0, fb0);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 6; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<16>();
+        wait_vmcnt<2 * COPIES>();
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
         read_frags(lds + ((kt + 1) & (STAGES - 1)) * STAGE_BYTES, 0, fa0, fb0);
         issue(kt + STAGES, slot);
         mma(fa1, fb1);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
+        for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one direct copy
+        }
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         }
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one direct load
-        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
         __builtin_amdgcn_sched_barrier(0);
     }
     // Peeled tail: at most STAGES - 1 stages with a successor, then the last.
@@ -334,8 +368,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1);
         mma(fa0, fb0);
         const int after = KT - 2 - kt;   // stages behind kt + 1 still in flight
-        if (after >= 2) wait_vmcnt<16>();
-        else if (after == 1) wait_vmcnt<8>();
+        if (after >= 2) wait_vmcnt<2 * COPIES>();
+        else if (after == 1) wait_vmcnt<COPIES>();
         else wait_vmcnt<0>();
         lds_barrier();
         read_frags(lds + ((kt + 1) & (STAGES - 1)) * STAGE_BYTES, 0, fa0, fb0);
@@ -345,49 +379,43 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     mma(fa0, fb0);
     mma(fa1, fb1);
 
-    // Epilogue.  Block (i, j), lane l, register r of the MFMA accumulators
-    // holds row 32 i + 8 (r / 4) + 4 (l / 32) + r % 4 and column 32 j + l % 32
-    // of the wave's 128 x 128 sub-tile.  Row block by row block, each wave
-    // parks its 32 x 128 int32 accumulators in its own quarter of the (now
-    // free) LDS ring, then reads them back row-contiguous: every lane takes 8
-    // consecutive columns of one row, applies the scales (loaded once) and
-    // the epilogue math in a compact loop, and writes one 16-byte store.
+    // Epilogue.  Block (a, b), lane l, register r of the MFMA accumulators
+    // holds row 32 a + 8 (r / 4) + 4 (l / 32) + r % 4 and column 32 b + l % 32
+    // of the wave's 64 x 128 sub-tile.  Row block by row block, each wave
+    // parks its 32 x 128 int32 accumulators in its own part of the (now free)
+    // ring, then reads them back row-contiguous: every lane takes 8
+    // consecutive columns of one row, applies the scales and the epilogue math
+    // in a compact loop, and writes one 16-byte store.
     lds_barrier();   // every wave is done reading the ring
-    int32_t* stash = reinterpret_cast<int32_t*>(lds + wave * (STAGES * STAGE_BYTES / 4));
-    constexpr int PITCH = 136;   // int32 per stashed row (bank-spread padding)
-    float* sxl = reinterpret_cast<float*>(stash + 32 * PITCH);   // the wave's 128 row scales
-    const bool full_tile_rows = m0 + BM <= M;
-    if constexpr (EP != Epilogue::S32) {
-        sxl[lane] = sx_pre0;
-        sxl[64 + lane] = sx_pre1;
-    }
+    int32_t* stash = reinterpret_cast<int32_t*>(lds + wave * STASH_WAVE_BYTES);
+    const int grow0 = m0 + 64 * wm;
 
-    auto stash_block = [&](int i) {
+    auto stash_block = [&](int a) {
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int b = 0; b < 4; ++b)
 #pragma unroll
             for (int r = 0; r < 16; ++r)
-                stash[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * PITCH + 32 * j + (lane & 31)] =
-                    acc[i][j][r];
+                stash[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * PITCH + 32 * b + (lane & 31)] =
+                    acc[a][b][r];
         asm volatile("" ::: "memory");
     };
 
     const int col0 = epi_col0;
     const int cg = epi_cg;
     const int ro = epi_ro;
-    const bool vec = full_tile_rows && (col0 + 8 <= N) && (N % 8 == 0);
+    const bool vec_cols = (col0 + 8 <= N) && (N % 8 == 0);
     if constexpr (EP == Epilogue::SWIGLU) {
         // lane -> 8 output columns (gate j, up i + j) and a row phase of 8
         uint16_t* y = reinterpret_cast<uint16_t*>(out);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            stash_block(i);
+        for (int a = 0; a < 2; ++a) {
+            stash_block(a);
 #pragma nounroll
             for (int it = 0; it < 4; ++it) {
                 const int lr = 8 * it + ro;
-                const int grow = grow0 + 32 * i + lr;
-                const float sxr = sxl[32 * i + lr];
+                const int grow = grow0 + 32 * a + lr;
+                const float sxr = sx_lds[64 * wm + 32 * a + lr];
                 const v4i g0 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg);
                 const v4i g1 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg + 4);
                 const v4i u0 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 64 + 8 * cg);
@@ -401,34 +429,37 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                     const float u = dequant(ua[e], sxr, swb[e]);
                     h[e] = bf16_rne((g / (1.0f + exp_cw(-g))) * u);
                 }
-                if (vec) {
-                    v4u pk = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                              h[6] | (h[7] << 16)};
-                    *reinterpret_cast<v4u*>(y + (int64_t)grow * N + col0) = pk;
-                } else if (grow < M) {
+                if (grow < M) {
+                    if (vec_cols) {
+                        v4u pk = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
+                                  h[6] | (h[7] << 16)};
+                        *reinterpret_cast<v4u*>(y + (int64_t)grow * N + col0) = pk;
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 8; ++e)
-                        if (col0 + e < N) y[(int64_t)grow * N + col0 + e] = (uint16_t)h[e];
+                        for (int e = 0; e < 8; ++e)
+                            if (col0 + e < N) y[(int64_t)grow * N + col0 + e] = (uint16_t)h[e];
+                    }
                 }
             }
         }
     } else {
         // lane -> 8 output columns and a row phase of 4
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            stash_block(i);
+        for (int a = 0; a < 2; ++a) {
+            stash_block(a);
 #pragma nounroll
             for (int it = 0; it < 8; ++it) {
                 const int lr = 4 * it + ro;
-                const int grow = grow0 + 32 * i + lr;
+                const int grow = grow0 + 32 * a + lr;
                 const v4i a0 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg);
                 const v4i a1 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg + 4);
+                if (grow >= M) continue;
                 if constexpr (EP == Epilogue::S32) {
                     int32_t* o = reinterpret_cast<int32_t*>(out);
-                    if (vec) {
+                    if (vec_cols) {
                         *reinterpret_cast<v4i*>(o + (int64_t)grow * N + col0) = a0;
                         *reinterpret_cast<v4i*>(o + (int64_t)grow * N + col0 + 4) = a1;
-                    } else if (grow < M) {
+                    } else {
                         const int av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
@@ -436,16 +467,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                     }
                 } else {
                     uint16_t* y = reinterpret_cast<uint16_t*>(out);
-                    const float sxr = sxl[32 * i + lr];
+                    const float sxr = sx_lds[64 * wm + 32 * a + lr];
                     const int av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
                     uint32_t h[8];
 #pragma unroll
                     for (int e = 0; e < 8; ++e) h[e] = bf16_rne(dequant(av[e], sxr, swa[e]));
-                    if (vec) {
+                    if (vec_cols) {
                         v4u pk = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
                                   h[6] | (h[7] << 16)};
                         *reinterpret_cast<v4u*>(y + (int64_t)grow * N + col0) = pk;
-                    } else if (grow < M) {
+                    } else {
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
                             if (col0 + e < N) y[(int64_t)grow * N + col0 + e] = (uint16_t)h[e];
