@@ -116,12 +116,13 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const int8_t* base, 
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN kept quiet); branch-free.
-__device__ __forceinline__ uint32_t bf16_rne(float f) {
-    const uint32_t u = __float_as_uint(f);
-    const uint32_t r = (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-    const uint32_t q = (u >> 16) | 0x0040u;
-    return ((u & 0x7fffffffu) > 0x7f800000u) ? q : r;
+// Two fp32 values -> packed bf16 bits (lo = a, hi = b), round to nearest
+// even: one v_cvt_pk_bf16_f32 on gfx950 (fp32 denormals are kept, so a
+// denormal product rounds to the bf16 denormal below or above it).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    const bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
 }
 
 // Fixed fp32 exponential (Cody-Waite reduction + degree-7 Taylor, fused
@@ -142,14 +143,16 @@ __device__ __forceinline__ float exp_cw_core(float x) {
     return __builtin_ldexpf(p, (int)kf);
 }
 
-// Evaluated branch-free: out-of-range arguments are replaced by 0 for the
-// polynomial and the result is selected afterwards (bit-identical in range).
-__device__ __forceinline__ float exp_cw(float x) {
-    const bool hi = x > 88.72f;
-    const bool lo = x < -86.0f;
-    const float xin = (hi || lo) ? 0.0f : x;
+// 1 + exp(x) as silu's denominator needs it, branch-free.  The fixed
+// exponential is +inf above 88.72 and 0 below -86.  Below -86 the polynomial
+// evaluated at the clamp point -86 gives about 4.4e-38, far below half an
+// ulp of 1 (2^-24), so 1 + that rounds to exactly 1, as 1 + 0 does; hence
+// clamping the argument into [-86, 88.72] with one med3 and selecting +inf
+// above the range reproduces the definition's 1 + exp(x) bit for bit.
+__device__ __forceinline__ float one_plus_exp_cw(float x) {
+    const float xin = __builtin_amdgcn_fmed3f(x, -86.0f, 88.72f);
     const float v = exp_cw_core(xin);
-    return hi ? __builtin_inff() : (lo ? 0.0f : v);
+    return 1.0f + (x > 88.72f ? __builtin_inff() : v);
 }
 
 __device__ __forceinline__ float dequant(int acc, float sx, float sw) {
@@ -422,22 +425,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                 const v4i u1 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 64 + 8 * cg + 4);
                 const int ga[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
                 const int ua[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-                uint32_t h[8];
+                float h[8];
 #pragma unroll
                 for (int e = 0; e < 8; ++e) {
                     const float g = dequant(ga[e], sxr, swa[e]);
                     const float u = dequant(ua[e], sxr, swb[e]);
-                    h[e] = bf16_rne((g / (1.0f + exp_cw(-g))) * u);
+                    h[e] = (g / one_plus_exp_cw(-g)) * u;
                 }
+                const v4u pk = {pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]), pack_bf16(h[4], h[5]),
+                                pack_bf16(h[6], h[7])};
                 if (grow < M) {
                     if (vec_cols) {
-                        v4u pk = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                                  h[6] | (h[7] << 16)};
                         *reinterpret_cast<v4u*>(y + (int64_t)grow * N + col0) = pk;
                     } else {
+                        const uint32_t pw[4] = {pk.x, pk.y, pk.z, pk.w};
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
-                            if (col0 + e < N) y[(int64_t)grow * N + col0 + e] = (uint16_t)h[e];
+                            if (col0 + e < N)
+                                y[(int64_t)grow * N + col0 + e] = (uint16_t)(pw[e >> 1] >> (16 * (e & 1)));
                     }
                 }
             }
@@ -469,17 +474,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                     uint16_t* y = reinterpret_cast<uint16_t*>(out);
                     const float sxr = sx_lds[64 * wm + 32 * a + lr];
                     const int av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-                    uint32_t h[8];
+                    float h[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) h[e] = bf16_rne(dequant(av[e], sxr, swa[e]));
+                    for (int e = 0; e < 8; ++e) h[e] = dequant(av[e], sxr, swa[e]);
+                    const v4u pk = {pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]), pack_bf16(h[4], h[5]),
+                                    pack_bf16(h[6], h[7])};
                     if (vec_cols) {
-                        v4u pk = {h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16),
-                                  h[6] | (h[7] << 16)};
                         *reinterpret_cast<v4u*>(y + (int64_t)grow * N + col0) = pk;
                     } else {
+                        const uint32_t pw[4] = {pk.x, pk.y, pk.z, pk.w};
 #pragma unroll
                         for (int e = 0; e < 8; ++e)
-                            if (col0 + e < N) y[(int64_t)grow * N + col0 + e] = (uint16_t)h[e];
+                            if (col0 + e < N)
+                                y[(int64_t)grow * N + col0 + e] = (uint16_t)(pw[e >> 1] >> (16 * (e & 1)));
                     }
                 }
             }

@@ -115,6 +115,33 @@ def test_degenerate_rows(cr):
     assert g["s_w"][0] == 0 and not g["q_w"][0].any()
 
 
+def test_bf16_rounding_edges(cr):
+    """The dequant epilogue's fp32 -> bf16 rounding on crafted values: one-hot
+    weight rows make every output a single product of two int8 codes (many
+    have 9+ significant bits, so exact half-way cases occur), and power-of-two
+    scales move the products through the fp32 denormal range and past the
+    largest finite value.  The oracle rounds half to even with denormals kept."""
+    import torch
+    rng = np.random.default_rng(23)
+    m, n, k = 96, 256, 256
+    qx = rng.integers(-127, 128, size=(m, k), dtype=np.int8)
+    codes = rng.integers(1, 128, size=n) * rng.choice([-1, 1], size=n)
+    qw = np.zeros((n, k), dtype=np.int8)
+    qw[np.arange(n), np.arange(n)] = codes
+    ex = rng.integers(-150, 30, size=m)
+    ex[:4] = [0, -126, -133, 113]             # exact ties, denormal edge, deep denormal, overflow
+    sx = np.ldexp(np.float32(1.0), ex).astype(np.float32)
+    sw = np.ldexp(np.float32(1.0), rng.integers(-8, 9, size=n)).astype(np.float32)
+    y = cr.gemm_dequant(gu.dev(qx), gu.dev(sx), gu.dev(qw), gu.dev(sw))
+    torch.cuda.synchronize()
+    acc = oracle.gemm_s32(qx, qw)
+    ref = oracle.dequant_bf16(acc, sx, sw)
+    got = gu.host_bf16(y)
+    f = (acc.astype(np.float64) * sx[:, None].astype(np.float64)) * sw[None, :].astype(np.float64)
+    assert np.any(np.abs(f) < 2.0 ** -126) and np.any(np.abs(f) > 3.4e38)   # both ranges are hit
+    gu.assert_equal(got, ref, "bf16 rounding edges")
+
+
 def test_tie_rows_half_even(cr):
     """Rows whose rotation is exactly a half-integer multiple of the scale
     (amax 127 s) round half to even on the GPU as in the oracle."""
