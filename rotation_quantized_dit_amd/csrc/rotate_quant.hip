@@ -272,8 +272,13 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_long_kernel(
 template <typename Tin>
 hipError_t launch(const Tin* x, int64_t rows, int64_t k, int8_t* q, float* s, hipStream_t stream) {
     const int G = (int)(k / 256);
-    // Prefer the fewest register-resident groups per slot, then the fewest waves.
-    const int P = (G + 4 * kMaxWaves - 1) / (4 * kMaxWaves);
+    // Register-resident groups per lane-slot: at least two once a row spans
+    // more than one wave's four groups (each lane then has two 16-element
+    // loads in flight and the row needs half the waves, so more rows fit on a
+    // CU: measured 1.8x faster for 21-group rows than one group per slot),
+    // and more only when 32 groups per pass would not cover the row.
+    int P = (G + 4 * kMaxWaves - 1) / (4 * kMaxWaves);
+    if (P == 1 && G > 4) P = 2;
     if (P <= kMaxPasses) {
         const int W = (G + 4 * P - 1) / (4 * P);
         dim3 block(64 * W);
