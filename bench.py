@@ -73,9 +73,10 @@ def measured_traffic(kernel):
     return fetch + write
 
 
-def cpu_baseline(x_bits, w_up, w_dn, target_s=12.0):
+def cpu_baseline(x_bits, w_up, w_dn, target_s=12.0, single_s=3.0):
     """The CPU oracle (as it stands) on a bounded sample of the same step:
-    the first R token rows through both layers."""
+    the first R token rows through both layers, on all of the host's threads
+    (OpenMP over rows) and, on a smaller sample, on one thread."""
     import oracle
     threads = oracle.get_threads()
     log("cpu baseline: oracle weight prep (untimed)")
@@ -96,10 +97,22 @@ def cpu_baseline(x_bits, w_up, w_dn, target_s=12.0):
     rows = max(r, min(8192, int(r * target_s / max(t, 1e-3))))
     log("cpu baseline: %d rows (probe %d rows took %.2f s)" % (rows, r, t))
     t = run(rows)
-    ops = 2.0 * rows * (n_up * k_up + n_dn * k_dn)
+    per_row_ops = 2.0 * (n_up * k_up + n_dn * k_dn)
+    ops = per_row_ops * rows
+    # one thread: rows sized from the all-threads rate for about single_s seconds
+    r1 = max(1, min(rows, int(single_s * rows / t / max(threads, 1))))
+    oracle.set_threads(1)
+    try:
+        t1 = run(r1)
+    finally:
+        oracle.set_threads(threads)
+    log("cpu baseline: %d rows on %d threads in %.1f s, %d rows on 1 thread in %.1f s" % (rows, threads, t, r1, t1))
     return {"value": ops / t / 1e12, "unit": "TOPS", "cores": threads, "kind": "oracle",
             "sample": "first %d of 32256 token rows through FFN-up+SwiGLU and FFN-down "
-                      "(rotate+quantize, int32 GEMM, epilogues), %.1f s" % (rows, t)}
+                      "(rotate+quantize, int32 GEMM, epilogues), %.1f s" % (rows, t),
+            "single_thread_value": per_row_ops * r1 / t1 / 1e12,
+            "single_thread_sample": "first %d rows, %.1f s" % (r1, t1),
+            "host_cpus": os.cpu_count()}
 
 
 def main():
@@ -202,6 +215,20 @@ def main():
     seg = np.array([[evs[i][j].elapsed_time(evs[i][j + 1]) for j in range(4)] for i in range(args.steps)])
     step_ms = np.array([evs[i][0].elapsed_time(evs[i][4]) for i in range(args.steps)])
     ms = float(step_ms.mean())
+
+    # Cold variant: before each timed step a 512 MiB scratch buffer is written,
+    # which evicts the previous step's weights and activations from the 256 MB
+    # Infinity Cache; only the step itself is inside the events.
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold_n = max(3, min(args.steps, 10))
+    cevs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(cold_n)]
+    for i in range(cold_n):
+        scratch.fill_(i & 0xff)
+        step(cevs[i])
+    torch.cuda.synchronize()
+    del scratch
+    cold_seg = np.array([[cevs[i][j].elapsed_time(cevs[i][j + 1]) for j in range(4)] for i in range(cold_n)])
+    cold_step = np.array([cevs[i][0].elapsed_time(cevs[i][4]) for i in range(cold_n)])
     ops_up = 2.0 * M * N1 * K1
     ops_dn = 2.0 * M * N2 * K2
     total_ops = ops_up + ops_dn
@@ -213,7 +240,9 @@ def main():
     names = ["rotate_quant_up", "gemm_swiglu_up", "rotate_quant_down", "gemm_dequant_down"]
     for j, name in enumerate(names):
         d = float(seg[:, j].mean())
-        e = {"ms": round(d, 4)}
+        e = {"ms": round(d, 4), "ms_median": round(float(np.median(seg[:, j])), 4),
+             "ms_min": round(float(seg[:, j].min()), 4), "ms_max": round(float(seg[:, j].max()), 4),
+             "ms_cold_median": round(float(np.median(cold_seg[:, j])), 4)}
         if name.startswith("rotate"):
             b = rot1_b if j == 0 else rot2_b
             e["GB/s"] = round(b / (d * 1e-3) / 1e9, 1)
@@ -257,6 +286,11 @@ def main():
                    "tokens": M, "hidden": K1, "ffn": I, "gemms": ["%dx%dx%d" % (M, N1, K1),
                                                                   "%dx%dx%d" % (M, N2, K2)]},
         "pct_int8_peak": round(100.0 * value / PEAK_INT8_TOPS, 2),
+        "step_ms": {"mean": round(ms, 4), "median": round(float(np.median(step_ms)), 4),
+                    "min": round(float(step_ms.min()), 4), "max": round(float(step_ms.max()), 4)},
+        "cold": {"steps": cold_n, "ms_per_step_median": round(float(np.median(cold_step)), 4),
+                 "value": round(total_ops / (float(np.median(cold_step)) * 1e-3) / 1e12, 2),
+                 "note": "512 MiB scratch written before each step (Infinity Cache evicted)"},
         "kernels": kern,
         "roofline": roofline,
         "cpu_baseline": cpu,
