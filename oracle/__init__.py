@@ -71,6 +71,9 @@ def lib() -> ctypes.CDLL:
         L.orc_silu.argtypes = [ctypes.c_float]
         L.orc_silu.restype = ctypes.c_float
         L.orc_swiglu_bf16.argtypes = [P, I64, I64, P, P, P]
+        L.orc_swiglu_pairs_bf16.argtypes = [P, I64, I64, P]
+        L.orc_swiglu_rotate_quant_rows.argtypes = [P, I64, P, I64, P, P]
+        L.orc_swiglu_rotate_quant_rows.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -225,6 +228,40 @@ def swiglu_bf16(acc: np.ndarray, s_x: np.ndarray, s_w: np.ndarray) -> np.ndarray
     y = np.empty((nrows, i), np.uint16)
     lib().orc_swiglu_bf16(_p(acc), nrows, i, _p(s_x), _p(s_w), _p(y))
     return y
+
+
+def swiglu_pairs_bf16(gu_bf16: np.ndarray) -> np.ndarray:
+    """h = bf16(silu(g) * u) from fc1's bf16 output [m, 2i]: g = columns
+    [0, i), u = columns [i, 2i), both widened exactly."""
+    gu_bf16 = np.ascontiguousarray(gu_bf16, dtype=np.uint16)
+    m, n2 = gu_bf16.shape
+    assert n2 % 2 == 0
+    i = n2 // 2
+    h = np.empty((m, i), np.uint16)
+    lib().orc_swiglu_pairs_bf16(_p(gu_bf16), m, i, _p(h))
+    return h
+
+
+def swiglu_rotate_quant_act(gu_bf16: np.ndarray, rows: np.ndarray | None = None):
+    """SwiGLU on fc1's bf16 output [m, 2i], then rotate along i and quantize
+    per token: the down projection's codes and scales with SwiGLU moved out
+    of fc1's epilogue.  With ``rows``, only those rows (in that order)."""
+    gu_bf16 = np.ascontiguousarray(gu_bf16, dtype=np.uint16)
+    m, n2 = gu_bf16.shape
+    assert n2 % 2 == 0
+    i = n2 // 2
+    if rows is None:
+        nrows, rp = m, None
+    else:
+        rows = np.ascontiguousarray(rows, dtype=np.int64)
+        assert rows.size == 0 or (rows.min() >= 0 and rows.max() < m)
+        nrows, rp = rows.size, _p(rows)
+    q = np.empty((nrows, i), np.int8)
+    s = np.empty(nrows, np.float32)
+    rc = lib().orc_swiglu_rotate_quant_rows(_p(gu_bf16), i, rp, nrows, _p(q), _p(s))
+    if rc != 0:
+        raise ValueError("oracle swiglu_rotate_quant_act failed (i=%d)" % i)
+    return q, s
 
 
 # ------------------------------------------------------------------ compositions

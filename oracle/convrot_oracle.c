@@ -315,3 +315,51 @@ void orc_swiglu_bf16(const int32_t* acc, int64_t nrows, int64_t i_width, const f
         }
     }
 }
+
+/* --------------------------------------------- SwiGLU on fc1's output side */
+
+/* SwiGLU placed on the output side of fc1 (hybrid model card, "Native NVFP4
+ * projection benchmarks": an "FFN output + SwiGLU" projection, i.e. SwiGLU
+ * applied to fc1's written output rather than inside its epilogue).  Reading:
+ * fc1 writes its dequantized gate and up columns as bf16 in one [rows, 2i]
+ * array, gate columns [0, i) and up columns [i, 2i); each is widened exactly
+ * and h = bf16(silu(g) * u), silu as in orc_silu. */
+static void swiglu_pairs_row(const uint16_t* gu, int64_t i_width, uint16_t* h) {
+    for (int64_t c = 0; c < i_width; ++c) {
+        float g = orc_bf16_to_f32_one(gu[c]);
+        float u = orc_bf16_to_f32_one(gu[i_width + c]);
+        h[c] = orc_f32_to_bf16_one(orc_silu(g) * u);
+    }
+}
+
+void orc_swiglu_pairs_bf16(const uint16_t* gu, int64_t nrows, int64_t i_width, uint16_t* h) {
+    int64_t j;
+#pragma omp parallel for schedule(static)
+    for (j = 0; j < nrows; ++j) swiglu_pairs_row(gu + j * 2 * i_width, i_width, h + j * i_width);
+}
+
+/* The down projection's activation preparation with SwiGLU moved in front
+ * of it: h of each selected row as in orc_swiglu_pairs_bf16, then the same
+ * widening, rotation and per-token quantization as orc_rotate_quant_act_rows
+ * (so the codes equal those of rotating and quantizing the bf16 SwiGLU
+ * output).  Output row j belongs to input row rows[j] (rows NULL: 0..n-1). */
+int orc_swiglu_rotate_quant_rows(const uint16_t* gu, int64_t i_width, const int64_t* rows,
+                                 int64_t nrows, int8_t* q, float* s) {
+    if (i_width <= 0 || i_width % ORC_GROUP) return -1;
+    int fail = 0;
+    int64_t j;
+#pragma omp parallel for schedule(static) reduction(| : fail)
+    for (j = 0; j < nrows; ++j) {
+        int64_t r = rows ? rows[j] : j;
+        uint16_t* h = (uint16_t*)malloc((size_t)i_width * sizeof(uint16_t));
+        float* row = (float*)malloc((size_t)i_width * sizeof(float));
+        if (!h || !row) { free(h); free(row); fail |= 1; continue; }
+        swiglu_pairs_row(gu + r * 2 * i_width, i_width, h);
+        orc_bf16_to_f32(h, row, i_width);
+        orc_rotate_row(row, i_width);
+        orc_quantize_row(row, i_width, q + j * i_width, s + j);
+        free(h);
+        free(row);
+    }
+    return fail ? -1 : 0;
+}

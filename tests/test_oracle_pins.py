@@ -540,3 +540,87 @@ def test_tiny_digest_unchanged():
     path = os.path.join(os.path.dirname(__file__), "golden", "tiny_oracle_digest.txt")
     want = dict(l.split() for l in open(path) if l.strip() and not l.startswith("#"))
     assert digests() == want
+
+
+# ------------------------------------------------- SwiGLU on fc1's output side
+
+def _bf16_from_f64(v):
+    """Round float64 values once to bf16 (torch's fp64 -> bf16 cast is a single
+    round-to-nearest-even from the exact fp64 value), as raw bits."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(v, dtype=np.float64)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def test_swiglu_pairs_against_fp64():
+    """h = bf16(silu(g) * u) on fc1's bf16 output: equal to an fp64 evaluation
+    rounded once to bf16, except where the fp64 value lies within the fp32
+    chain's error (exp <= 1 ulp, then one add, one division and one multiply,
+    each RN) of a bf16 half-way point, where the neighbour is allowed.  Gate
+    columns [0, i), up columns [i, 2i): a swapped half fails by far."""
+    rng = np.random.default_rng(31)
+    m, i = 24, 512
+    g = rng.standard_normal((m, i)) * np.array([0.5, 4.0, 30.0])[rng.integers(0, 3, (m, i))]
+    u = rng.standard_normal((m, i)) * 3.0
+    gu = workloads.to_bf16_bits(np.concatenate([g, u], axis=1).astype(np.float32))
+    h = oracle.swiglu_pairs_bf16(gu)
+    gf = oracle.bf16_to_f32(gu[:, :i]).astype(np.float64)
+    uf = oracle.bf16_to_f32(gu[:, i:]).astype(np.float64)
+    with np.errstate(over="ignore"):
+        sil64 = gf / (1.0 + np.exp(-gf))
+    h64 = sil64 * uf
+    ref = _bf16_from_f64(h64)
+    hv = oracle.bf16_to_f32(h).astype(np.float64)
+    # fp32 exp(-g) overflows above 88.72, so the definition's fp32 quotient is
+    # exactly +-0 there (fp64 still has a denormal-range value)
+    over = -gf > 88.72
+    assert over.any() and np.all(hv[over] == 0) and np.all(np.abs(h64[over]) < 2.0 ** -100)
+    # where the quotient itself is near or inside the fp32 denormal range it
+    # carries fewer bits: its absolute error is at most a few denormal steps
+    # (2^-149), scaled by |u|, plus the final bf16 rounding of the product
+    tiny = ~over & (np.abs(sil64) < 2.0 ** -120)
+    assert tiny.any()
+    bound = np.abs(uf) * 2.0 ** -147 + 2.0 ** -8 * np.abs(h64) + 2.0 ** -133
+    assert np.all(np.abs(hv[tiny] - h64[tiny]) <= bound[tiny])
+    diff = (h != ref) & ~over & ~tiny
+    assert diff.mean() < 1e-3, diff.mean()
+    # every other mismatch is a near-tie: h64 within 8 fp32 ulps of the bf16 midpoint between the two
+    for r, c in zip(*np.nonzero(diff)):
+        a = float(oracle.bf16_to_f32(np.array([h[r, c]], np.uint16))[0])
+        b = float(oracle.bf16_to_f32(np.array([ref[r, c]], np.uint16))[0])
+        assert abs(np.int32(h[r, c]) - np.int32(ref[r, c])) == 1       # adjacent bf16 values
+        mid = 0.5 * (a + b)
+        assert abs(h64[r, c] - mid) <= 8 * U * abs(mid), (h64[r, c], a, b)
+    # the halves matter: silu(u) * g differs almost everywhere
+    with np.errstate(over="ignore"):
+        swapped = _bf16_from_f64(uf / (1.0 + np.exp(-uf)) * gf)
+    assert (swapped != h).mean() > 0.9
+
+
+def test_swiglu_pairs_special_values():
+    """silu(0) u = 0; u = 0 gives 0; g -> -inf gives -0 (1 + e^200 overflows);
+    large g gives silu(g) = g exactly (e^-g is 0 below -86), so h = bf16(g u)."""
+    g = np.array([0.0, 1.5, -200.0, 200.0, 120.0, -3.0], np.float32)
+    u = np.array([5.0, 0.0, 2.0, 2.0, -0.5, 0.0], np.float32)
+    gu = workloads.to_bf16_bits(np.concatenate([g, u])[None, :])
+    h = oracle.bf16_to_f32(oracle.swiglu_pairs_bf16(gu))[0]
+    assert h[0] == 0 and h[1] == 0 and h[5] == 0
+    assert h[2] == 0 and np.signbit(h[2])          # (-200 / inf) * 2 = -0
+    assert h[3] == 400.0 and h[4] == -60.0
+
+
+def test_swiglu_rotate_quant_composes():
+    """The fused preparation equals rotating and quantizing the bf16 SwiGLU
+    output row by row (selected rows included), and a row whose up half is
+    zero has scale 0 and all-zero codes."""
+    rng = np.random.default_rng(32)
+    m, i = 9, 768
+    gu = workloads.to_bf16_bits(rng.laplace(size=(m, 2 * i)).astype(np.float32))
+    gu[3, i:] = 0
+    q, s = oracle.swiglu_rotate_quant_act(gu)
+    q2, s2 = oracle.rotate_quant_act(oracle.swiglu_pairs_bf16(gu))
+    assert np.array_equal(q, q2) and np.array_equal(s.view(np.uint32), s2.view(np.uint32))
+    assert s[3] == 0 and not q[3].any()
+    rows = np.array([8, 3, 0])
+    qr, sr = oracle.swiglu_rotate_quant_act(gu, rows)
+    assert np.array_equal(qr, q[rows]) and np.array_equal(sr, s[rows])
