@@ -253,6 +253,53 @@ def main():
             e["pct_int8_peak"] = round(100.0 * o / (d * 1e-3) / 1e12 / PEAK_INT8_TOPS, 1)
         kern[name] = e
 
+    # The same FFN with SwiGLU on fc1's output side: fc1 writes bf16 gate/up
+    # [M, 2I] (dequant epilogue), one pass forms h and rotates + quantizes it,
+    # then the same down GEMM.  Same inputs, weights and outputs sizes.
+    gu_buf = torch.empty((M, N1), dtype=torch.bfloat16, device=dev)
+
+    def step_out(ev=None):
+        if ev:
+            ev[0].record()
+        cr.rotate_quant_act(x, qx1, sx1)
+        if ev:
+            ev[1].record()
+        cr.gemm_dequant(qx1, sx1, qwu, swu, out=gu_buf)
+        if ev:
+            ev[2].record()
+        cr.swiglu_rotate_quant_act(gu_buf, qx2, sx2)
+        if ev:
+            ev[3].record()
+        cr.gemm_dequant(qx2, sx2, qwd, swd, out=y)
+        if ev:
+            ev[4].record()
+
+    for _ in range(args.warmup):
+        step_out()
+    oevs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        step_out(oevs[i])
+    torch.cuda.synchronize()
+    del gu_buf
+    oseg = np.array([[oevs[i][j].elapsed_time(oevs[i][j + 1]) for j in range(4)] for i in range(args.steps)])
+    ostep = np.array([oevs[i][0].elapsed_time(oevs[i][4]) for i in range(args.steps)])
+    gu_bytes = 2.0 * M * N1
+    out_side = {
+        "ms_per_step": round(float(ostep.mean()), 4),
+        "value": round(total_ops / (float(ostep.mean()) * 1e-3) / 1e12, 2),
+        "kernels": {
+            "rotate_quant_up": {"ms": round(float(oseg[:, 0].mean()), 4)},
+            "gemm_dequant_up_2I": {"ms": round(float(oseg[:, 1].mean()), 4),
+                                   "TOPS": round(ops_up / (float(oseg[:, 1].mean()) * 1e-3) / 1e12, 1)},
+            "swiglu_rotate_quant_down": {"ms": round(float(oseg[:, 2].mean()), 4),
+                                         "GB/s": round((gu_bytes + M * K2 + 4.0 * M) /
+                                                       (float(oseg[:, 2].mean()) * 1e-3) / 1e9, 1)},
+            "gemm_dequant_down": {"ms": round(float(oseg[:, 3].mean()), 4)},
+        },
+        "note": "SwiGLU on fc1's output side: fc1 writes bf16 gate/up [M, 2I]; one pass forms h, "
+                "rotates and quantizes it",
+    }
+
     # cross-check: the same step through the fused entry points (same kernels)
     torch.cuda.synchronize()
     ws = torch.empty(max(cr.workspace_bytes(M, K1), cr.workspace_bytes(M, K2)), dtype=torch.uint8, device=dev)
@@ -295,6 +342,7 @@ def main():
         "roofline": roofline,
         "cpu_baseline": cpu,
         "fused_api_ms_per_step": round(fused_ms, 4),
+        "output_side_swiglu": out_side,
         "weight_quant": {"ms": round(wq_ms, 4), "GB/s": round(wq_bytes / (wq_ms * 1e-3) / 1e9, 1)},
         "wall_s": round(wall, 3),
     }

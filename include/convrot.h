@@ -97,6 +97,19 @@ int convrot_quantize_weight(const float* w, int64_t n, int64_t k,
 int convrot_rotate_quant_act(const uint16_t* x, int64_t m, int64_t k,
                              int8_t* q_x, float* s_x, void* stream);
 
+/* The down projection's activation preparation with SwiGLU applied in front
+ * of the rotation instead of in fc1's epilogue (Minimax_h3_hybrid model card,
+ * "Native NVFP4 projection benchmarks": an "FFN output + SwiGLU" projection).
+ * fc1 writes its dequantized gate and up columns as bf16 (convrot_linear with
+ * n = 2i); this pass forms h = bf16(silu(g) * u), silu(g) = g / (1 + exp(-g))
+ * with the same fixed exponential as the SwiGLU epilogue, widens h exactly,
+ * and rotates and quantizes it per token as convrot_rotate_quant_act does.
+ *   gu   [m, 2i] bf16: columns [0, i) gate, columns [i, 2i) up
+ *   q_h  [m, i]  int8 output codes;  s_h [m] fp32 output per-token scales
+ * i is the down projection's k: i % 256 == 0, i <= CONVROT_MAX_K.            */
+int convrot_swiglu_rotate_quant_act(const uint16_t* gu, int64_t m, int64_t i,
+                                    int8_t* q_h, float* s_h, void* stream);
+
 /* Workspace that convrot_linear / convrot_linear_swiglu need for m tokens of
  * length k: q_x at offset 0 (m * k bytes), then s_x at offset m * k (4 * m
  * bytes; 256-byte aligned whenever the workspace is, since k % 256 == 0).

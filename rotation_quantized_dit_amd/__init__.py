@@ -20,5 +20,6 @@ from ._lib import (  # noqa: F401
     quantize_weight,
     rotate_quant_act,
     status_string,
+    swiglu_rotate_quant_act,
     workspace_bytes,
 )

@@ -25,7 +25,7 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH = range(6)
 SYMBOLS = (
     "convrot_quantize_weight", "convrot_rotate_quant_act", "convrot_workspace_bytes",
     "convrot_linear", "convrot_linear_swiglu", "convrot_gemm_dequant", "convrot_gemm_swiglu",
-    "convrot_gemm_s32", "convrot_status_string",
+    "convrot_gemm_s32", "convrot_swiglu_rotate_quant_act", "convrot_status_string",
 )
 
 
@@ -53,6 +53,7 @@ def load_library() -> ctypes.CDLL:
         sig = {
             "convrot_quantize_weight": ([P, I64, I64, P, P, P], I),
             "convrot_rotate_quant_act": ([P, I64, I64, P, P, P], I),
+            "convrot_swiglu_rotate_quant_act": ([P, I64, I64, P, P, P], I),
             "convrot_workspace_bytes": ([I64, I64], SZ),
             "convrot_linear": ([P, I64, I64, P, P, I64, P, P, SZ, P], I),
             "convrot_linear_swiglu": ([P, I64, I64, P, P, I64, P, P, SZ, P], I),
@@ -128,6 +129,22 @@ def rotate_quant_act(x: torch.Tensor, q_x=None, s_x=None):
     _check("convrot_rotate_quant_act", load_library().convrot_rotate_quant_act(
         x.data_ptr(), m, k, q_x.data_ptr(), s_x.data_ptr(), _stream()))
     return q_x, s_x
+
+
+def swiglu_rotate_quant_act(gu: torch.Tensor, q_h=None, s_h=None):
+    """fc1's bf16 output gu [m, 2i] (gate columns [0, i), up [i, 2i)) ->
+    codes [m, i] and per-token scales [m] of h = bf16(silu(gate) * up),
+    rotated and quantized as rotate_quant_act does."""
+    _dev(gu, "gu", torch.bfloat16, 2)
+    m, n2 = gu.shape
+    if n2 % 2:
+        raise ValueError("gu must have an even number of columns (got %d)" % n2)
+    i = n2 // 2
+    q_h = _out(q_h, (m, i), torch.int8, gu, "q_h")
+    s_h = _out(s_h, (m,), torch.float32, gu, "s_h")
+    _check("convrot_swiglu_rotate_quant_act", load_library().convrot_swiglu_rotate_quant_act(
+        gu.data_ptr(), m, i, q_h.data_ptr(), s_h.data_ptr(), _stream()))
+    return q_h, s_h
 
 
 def _workspace(workspace, m, k, like):

@@ -97,6 +97,16 @@ int convrot_rotate_quant_act(const uint16_t* x, int64_t m, int64_t k, int8_t* q_
     return launched(convrot::launch_rotate_quant_bf16(x, m, k, q_x, s_x, (hipStream_t)stream));
 }
 
+int convrot_swiglu_rotate_quant_act(const uint16_t* gu, int64_t m, int64_t i, int8_t* q_h,
+                                    float* s_h, void* stream) {
+    int st;
+    if ((st = check_rows(m)) || (st = check_k(i))) return st;
+    if (m == 0) return CONVROT_OK;
+    if (!gu || !q_h || !s_h) return CONVROT_ERR_NULL;
+    if (!aligned16(gu) || !aligned16(q_h) || !aligned16(s_h)) return CONVROT_ERR_ALIGN;
+    return launched(convrot::launch_swiglu_rotate_quant(gu, m, i, q_h, s_h, (hipStream_t)stream));
+}
+
 int convrot_gemm_s32(const int8_t* q_x, const int8_t* q_w, int64_t m, int64_t n, int64_t k,
                      int32_t* acc, void* stream) {
     int st = check_gemm_shape(m, n, n, k);

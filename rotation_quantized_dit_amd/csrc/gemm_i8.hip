@@ -48,6 +48,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fixed_math.h"
 #include "kernels.h"
 
 namespace convrot {
@@ -114,45 +115,6 @@ __device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t rsrc, int8_t* dst,
 // Buffer resource over [base, base + bytes) (raw, no stride; gfx9 dword 3).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const int8_t* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
-}
-
-// Two fp32 values -> packed bf16 bits (lo = a, hi = b), round to nearest
-// even: one v_cvt_pk_bf16_f32 on gfx950 (fp32 denormals are kept, so a
-// denormal product rounds to the bf16 denormal below or above it).
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    const bf16x2 v = {(__bf16)a, (__bf16)b};
-    return __builtin_bit_cast(uint32_t, v);
-}
-
-// Fixed fp32 exponential (Cody-Waite reduction + degree-7 Taylor, fused
-// multiply-adds, exact 2^k scaling); the same algorithm the layer's
-// definition fixes, evaluated op for op.
-__device__ __forceinline__ float exp_cw_core(float x) {
-    const float kf = __builtin_rintf(x * 0x1.715476p+0f);
-    float r = __builtin_fmaf(-kf, 0x1.62e4p-1f, x);
-    r = __builtin_fmaf(-kf, 0x1.7f7d1cp-20f, r);
-    float p = 0x1.a01a02p-13f;
-    p = __builtin_fmaf(p, r, 0x1.6c16c2p-10f);
-    p = __builtin_fmaf(p, r, 0x1.111112p-7f);
-    p = __builtin_fmaf(p, r, 0x1.555556p-5f);
-    p = __builtin_fmaf(p, r, 0x1.555556p-3f);
-    p = __builtin_fmaf(p, r, 0.5f);
-    p = __builtin_fmaf(p, r, 1.0f);
-    p = __builtin_fmaf(p, r, 1.0f);
-    return __builtin_ldexpf(p, (int)kf);
-}
-
-// 1 + exp(x) as silu's denominator needs it, branch-free.  The fixed
-// exponential is +inf above 88.72 and 0 below -86.  Below -86 the polynomial
-// evaluated at the clamp point -86 gives about 4.4e-38, far below half an
-// ulp of 1 (2^-24), so 1 + that rounds to exactly 1, as 1 + 0 does; hence
-// clamping the argument into [-86, 88.72] with one med3 and selecting +inf
-// above the range reproduces the definition's 1 + exp(x) bit for bit.
-__device__ __forceinline__ float one_plus_exp_cw(float x) {
-    const float xin = __builtin_amdgcn_fmed3f(x, -86.0f, 88.72f);
-    const float v = exp_cw_core(xin);
-    return 1.0f + (x > 88.72f ? __builtin_inff() : v);
 }
 
 __device__ __forceinline__ float dequant(int acc, float sx, float sw) {
@@ -430,7 +392,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                 for (int e = 0; e < 8; ++e) {
                     const float g = dequant(ga[e], sxr, swa[e]);
                     const float u = dequant(ua[e], sxr, swb[e]);
-                    h[e] = (g / one_plus_exp_cw(-g)) * u;
+                    h[e] = swiglu_f32(g, u);
                 }
                 const v4u pk = {pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]), pack_bf16(h[4], h[5]),
                                 pack_bf16(h[6], h[7])};

@@ -12,6 +12,10 @@ hipError_t launch_rotate_quant_bf16(const uint16_t* x, int64_t rows, int64_t k, 
                                     float* s, hipStream_t stream);
 hipError_t launch_rotate_quant_f32(const float* x, int64_t rows, int64_t k, int8_t* q,
                                    float* s, hipStream_t stream);
+// The same pass on h = bf16(silu(g) * u) formed from fc1's bf16 output
+// gu [rows, 2i] (gate columns [0, i), up columns [i, 2i)); q is [rows, i].
+hipError_t launch_swiglu_rotate_quant(const uint16_t* gu, int64_t rows, int64_t i, int8_t* q,
+                                      float* s, hipStream_t stream);
 
 // K-GEMM: int8 x int8 -> int32 on MFMA with one of three epilogues.
 enum class Epilogue { S32, BF16, SWIGLU };

@@ -11,6 +11,10 @@
 //            one RNE add or subtract;
 //   s      = max |v| / 127 (correctly rounded);
 //   q      = rint(v / s) with a correctly rounded quotient, half to even.
+// The row comes from one of three sources: bf16 activations, fp32 weights
+// (load time), or fc1's bf16 gate/up output, from which the source forms
+// h = bf16(silu(g) * u) element by element before the rotation (SwiGLU moved
+// from fc1's epilogue to the front of the down projection's quantizer).
 //
 // Layout of the work.  One workgroup per row.  A 256-element group is handled
 // by 16 lanes; lane b of the 16 loads the 16 contiguous elements of block b
@@ -40,6 +44,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fixed_math.h"
 #include "kernels.h"
 
 namespace convrot {
@@ -75,6 +80,42 @@ __device__ __forceinline__ void load16(const float* __restrict__ p, float v[16])
         v[4 * i + 3] = t.w;
     }
 }
+
+// Input sources: how a lane obtains the 16 fp32 values at element offset
+// off (a multiple of 16) of row `row` of a k-wide input.
+struct Bf16Rows {   // activations, bf16 [rows, k]
+    const uint16_t* x;
+    __device__ __forceinline__ void load(int64_t row, int64_t k, int64_t off, float v[16]) const {
+        load16(x + row * k + off, v);
+    }
+};
+
+struct F32Rows {    // weights, fp32 [rows, k]
+    const float* x;
+    __device__ __forceinline__ void load(int64_t row, int64_t k, int64_t off, float v[16]) const {
+        load16(x + row * k + off, v);
+    }
+};
+
+// SwiGLU on fc1's bf16 output [rows, 2k] (hybrid model card, "Native NVFP4
+// projection benchmarks": an "FFN output + SwiGLU" projection): gate columns
+// [0, k), up columns [k, 2k), h = bf16(silu(g) * u), widened exactly; the
+// rotation then runs on h as on any bf16 activation row.
+struct SwiGluRows {
+    const uint16_t* gu;
+    __device__ __forceinline__ void load(int64_t row, int64_t k, int64_t off, float v[16]) const {
+        const uint16_t* r = gu + row * 2 * k;
+        float g[16], u[16];
+        load16(r + off, g);
+        load16(r + k + off, u);
+#pragma unroll
+        for (int e = 0; e < 16; e += 2) {
+            const uint32_t b = pack_bf16(swiglu_f32(g[e], u[e]), swiglu_f32(g[e + 1], u[e + 1]));
+            v[e] = __uint_as_float(b << 16);
+            v[e + 1] = __uint_as_float(b & 0xffff0000u);
+        }
+    }
+};
 
 // Four butterfly stages on 16 registers: spans 1, 2, 4, 8 of the index.
 __device__ __forceinline__ void butterfly16(float v[16]) {
@@ -153,9 +194,9 @@ __device__ __forceinline__ void quant_store(float* tile, int j, const float t[16
 // and P passes of the row in registers; all of a lane's loads are issued
 // before any transform.  The row maximum goes through LDS (one workgroup
 // barrier per row).
-template <typename Tin, int P>
+template <typename Src, int P>
 __global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_rows_kernel(
-    const Tin* __restrict__ x, int64_t k, int8_t* __restrict__ q, float* __restrict__ s_out) {
+    Src src, int64_t k, int8_t* __restrict__ q, float* __restrict__ s_out) {
     extern __shared__ float smem[];
     __shared__ float red[kMaxWaves];
     const int64_t row = blockIdx.x;
@@ -165,7 +206,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_rows_kernel(
     const int lane = threadIdx.x & 63;
     const int sub = lane >> 4;
     const int j = lane & 15;
-    const Tin* xr = x + row * k;
     int8_t* qr = q + row * k;
     float* tile = smem + wave * kWaveFloats + sub * kTile;
 
@@ -174,7 +214,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_rows_kernel(
     for (int p = 0; p < P; ++p) {
         const int g = (p * W + wave) * 4 + sub;
         if (g < G) {
-            load16(xr + (int64_t)g * 256 + j * 16, vals[p]);
+            src.load(row, k, (int64_t)g * 256 + j * 16, vals[p]);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) vals[p][i] = 0.0f;
@@ -210,10 +250,9 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_rows_kernel(
 // Rows longer than 32 W groups: one workgroup per row, the rotation is
 // computed twice (once for the row maximum, once to quantize) rather than
 // held in registers.
-template <typename Tin>
+template <typename Src>
 __global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_long_kernel(
-    const Tin* __restrict__ x, int64_t k, int passes, int8_t* __restrict__ q,
-    float* __restrict__ s_out) {
+    Src src, int64_t k, int passes, int8_t* __restrict__ q, float* __restrict__ s_out) {
     extern __shared__ float smem[];
     __shared__ float red[kMaxWaves];
     const int64_t row = blockIdx.x;
@@ -223,7 +262,6 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_long_kernel(
     const int lane = threadIdx.x & 63;
     const int sub = lane >> 4;
     const int j = lane & 15;
-    const Tin* xr = x + row * k;
     int8_t* qr = q + row * k;
     float* tile = smem + wave * kWaveFloats + sub * kTile;
 
@@ -232,7 +270,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_long_kernel(
         const int g = (p * W + wave) * 4 + sub;
         float t[16];
         if (g < G) {
-            load16(xr + (int64_t)g * 256 + j * 16, t);
+            src.load(row, k, (int64_t)g * 256 + j * 16, t);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) t[i] = 0.0f;
@@ -258,7 +296,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_long_kernel(
         const int g = (p * W + wave) * 4 + sub;
         float t[16];
         if (g < G) {
-            load16(xr + (int64_t)g * 256 + j * 16, t);
+            src.load(row, k, (int64_t)g * 256 + j * 16, t);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) t[i] = 0.0f;
@@ -269,8 +307,8 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_long_kernel(
     }
 }
 
-template <typename Tin>
-hipError_t launch(const Tin* x, int64_t rows, int64_t k, int8_t* q, float* s, hipStream_t stream) {
+template <typename Src>
+hipError_t launch(Src src, int64_t rows, int64_t k, int8_t* q, float* s, hipStream_t stream) {
     const int G = (int)(k / 256);
     // Register-resident groups per lane-slot: at least two once a row spans
     // more than one wave's four groups (each lane then has two 16-element
@@ -285,16 +323,16 @@ hipError_t launch(const Tin* x, int64_t rows, int64_t k, int8_t* q, float* s, hi
         const size_t lds = (size_t)W * kWaveFloats * sizeof(float);
         dim3 grid((unsigned)rows);
         switch (P) {
-            case 1: rotate_quant_rows_kernel<Tin, 1><<<grid, block, lds, stream>>>(x, k, q, s); break;
-            case 2: rotate_quant_rows_kernel<Tin, 2><<<grid, block, lds, stream>>>(x, k, q, s); break;
-            case 3: rotate_quant_rows_kernel<Tin, 3><<<grid, block, lds, stream>>>(x, k, q, s); break;
-            default: rotate_quant_rows_kernel<Tin, 4><<<grid, block, lds, stream>>>(x, k, q, s); break;
+            case 1: rotate_quant_rows_kernel<Src, 1><<<grid, block, lds, stream>>>(src, k, q, s); break;
+            case 2: rotate_quant_rows_kernel<Src, 2><<<grid, block, lds, stream>>>(src, k, q, s); break;
+            case 3: rotate_quant_rows_kernel<Src, 3><<<grid, block, lds, stream>>>(src, k, q, s); break;
+            default: rotate_quant_rows_kernel<Src, 4><<<grid, block, lds, stream>>>(src, k, q, s); break;
         }
     } else {
         dim3 grid((unsigned)rows);
         dim3 block(64 * kMaxWaves);
         const size_t lds = (size_t)kMaxWaves * kWaveFloats * sizeof(float);
-        rotate_quant_long_kernel<Tin><<<grid, block, lds, stream>>>(x, k, P, q, s);
+        rotate_quant_long_kernel<Src><<<grid, block, lds, stream>>>(src, k, P, q, s);
     }
     return hipGetLastError();
 }
@@ -303,12 +341,17 @@ hipError_t launch(const Tin* x, int64_t rows, int64_t k, int8_t* q, float* s, hi
 
 hipError_t launch_rotate_quant_bf16(const uint16_t* x, int64_t rows, int64_t k, int8_t* q,
                                     float* s, hipStream_t stream) {
-    return launch(x, rows, k, q, s, stream);
+    return launch(Bf16Rows{x}, rows, k, q, s, stream);
 }
 
 hipError_t launch_rotate_quant_f32(const float* x, int64_t rows, int64_t k, int8_t* q, float* s,
                                    hipStream_t stream) {
-    return launch(x, rows, k, q, s, stream);
+    return launch(F32Rows{x}, rows, k, q, s, stream);
+}
+
+hipError_t launch_swiglu_rotate_quant(const uint16_t* gu, int64_t rows, int64_t i, int8_t* q,
+                                      float* s, hipStream_t stream) {
+    return launch(SwiGluRows{gu}, rows, i, q, s, stream);
 }
 
 }  // namespace convrot

@@ -80,6 +80,7 @@ def test_k_bounds(L):
         assert L.convrot_quantize_weight(A, 4, k, B, C, None) == ERR_SHAPE, k
         assert L.convrot_gemm_s32(A, B, 4, 4, k, C, None) == ERR_SHAPE, k
         assert L.convrot_linear(A, 4, k, B, C, 4, D, A, 1 << 30, None) == ERR_SHAPE, k
+        assert L.convrot_swiglu_rotate_quant_act(A, 4, k, B, C, None) == ERR_SHAPE, k
 
 
 def test_negative_sizes(L):
@@ -93,6 +94,7 @@ def test_negative_sizes(L):
     assert L.convrot_linear(A, 4, 256, B, C, -1, D, A, 1 << 20, None) == ERR_SHAPE
     assert L.convrot_linear_swiglu(A, 4, 256, B, C, -3, D, A, 1 << 20, None) == ERR_SHAPE
     assert L.convrot_rotate_quant_act(A, 1 << 32, 256, B, C, None) == ERR_SHAPE
+    assert L.convrot_swiglu_rotate_quant_act(A, -1, 256, B, C, None) == ERR_SHAPE
 
 
 def test_null_pointers(L):
@@ -108,6 +110,9 @@ def test_null_pointers(L):
     assert L.convrot_gemm_swiglu(A, B, None, D, 4, 4, 256, A, None) == ERR_NULL
     assert L.convrot_linear(A, 4, 256, B, None, 4, D, A, 1 << 20, None) == ERR_NULL
     assert L.convrot_linear_swiglu(A, 4, 256, B, C, 4, None, A, 1 << 20, None) == ERR_NULL
+    assert L.convrot_swiglu_rotate_quant_act(None, 4, 256, B, C, None) == ERR_NULL
+    assert L.convrot_swiglu_rotate_quant_act(A, 4, 256, None, C, None) == ERR_NULL
+    assert L.convrot_swiglu_rotate_quant_act(A, 4, 256, B, None, None) == ERR_NULL
 
 
 def test_alignment(L):
@@ -118,6 +123,8 @@ def test_alignment(L):
     assert L.convrot_gemm_s32(A, B + 2, 4, 4, 256, C, None) == ERR_ALIGN
     assert L.convrot_gemm_dequant(A, B, C, D, 4, 4, 256, A + 8, None) == ERR_ALIGN
     assert L.convrot_linear(A, 4, 256, B, C, 4, D, MIS, 1 << 20, None) == ERR_ALIGN
+    assert L.convrot_swiglu_rotate_quant_act(MIS, 4, 256, B, C, None) == ERR_ALIGN
+    assert L.convrot_swiglu_rotate_quant_act(A, 4, 256, B, C + 4, None) == ERR_ALIGN
 
 
 def test_workspace_checks(L):
@@ -139,6 +146,7 @@ def test_zero_sizes_are_noops(L):
     assert L.convrot_gemm_swiglu(A, B, C, D, 4, 0, 256, A, None) == OK
     assert L.convrot_linear(A, 0, 256, B, C, 4, D, None, 0, None) == OK
     assert L.convrot_linear_swiglu(A, 7, 256, B, C, 0, D, None, 0, None) == OK
+    assert L.convrot_swiglu_rotate_quant_act(None, 0, 512, None, None, None) == OK
     # empty calls may pass NULL (torch's empty tensors do), but bad shapes still fail
     assert L.convrot_rotate_quant_act(None, 0, 256, None, None, None) == OK
     assert L.convrot_gemm_s32(None, None, 0, 0, 256, None, None) == OK

@@ -57,7 +57,15 @@ def _run_linear_workload(cr, name):
     ridx = torch.from_numpy(rows).cuda()
     g = dict(q_w=gu.host(qw_d), s_w=gu.host(sw_d), q_x=gu.host(qx_d), s_x=gu.host(sx_d),
              acc=acc_rows, y=gu.host_bf16(y_d[ridx]), y2=gu.host_bf16(y2_d[ridx]))
-    del y_d, y2_d, qx_d, qw_d, xd, wd
+    del y_d, y2_d
+    if c.swiglu:
+        # SwiGLU on fc1's output side: fc1 writes bf16 gate/up [M, 2I], then one
+        # pass forms h, rotates and quantizes it for the down projection
+        gu_d = cr.gemm_dequant(qx_d, sx_d, qw_d, sw_d)
+        qh_d, sh_d = cr.swiglu_rotate_quant_act(gu_d)
+        g.update(gu=gu.host_bf16(gu_d[ridx]), q_h=gu.host(qh_d[ridx]), s_h=gu.host(sh_d[ridx]))
+        del gu_d, qh_d, sh_d
+    del qx_d, qw_d, xd, wd
     torch.cuda.synchronize()
     print("%s: oracle" % name, flush=True)
     oqw, osw = oracle.quantize_weight(d["w"])
@@ -65,6 +73,9 @@ def _run_linear_workload(cr, name):
     acc = oracle.gemm_s32(oqx[rows], oqw)
     y = oracle.swiglu_bf16(acc, osx[rows], osw) if c.swiglu else oracle.dequant_bf16(acc, osx[rows], osw)
     o = dict(q_w=oqw, s_w=osw, q_x=oqx, s_x=osx, acc=acc, y=y)
+    if c.swiglu:
+        o["gu"] = oracle.dequant_bf16(acc, osx[rows], osw)
+        o["q_h"], o["s_h"] = oracle.swiglu_rotate_quant_act(o["gu"])
     return g, o, rows
 
 
@@ -112,6 +123,16 @@ def test_ffn_up_swiglu_codes(ffn_up):
 
 def test_ffn_up_swiglu_outputs(ffn_up):
     _check_outputs(ffn_up, "ffn_up")
+
+
+def test_ffn_up_output_side_swiglu(ffn_up):
+    """fc1 with the bf16 dequant epilogue on all 2 x 14336 columns, then SwiGLU
+    + rotate + quantize in one pass: the bf16 gate/up rows and the down
+    projection's codes and scales match the oracle bit for bit (sampled rows)."""
+    g, o, _ = ffn_up
+    gu.assert_bf16_parity(g["gu"], o["gu"], "ffn_up fc1 bf16 gate/up (sampled rows)")
+    gu.assert_equal(g["q_h"], o["q_h"], "ffn_up output-side SwiGLU q_h (sampled rows)")
+    gu.assert_equal(_f32_bits(g["s_h"]), _f32_bits(o["s_h"]), "ffn_up output-side SwiGLU s_h (sampled rows)")
 
 
 def test_ffn_down_codes(ffn_down):

@@ -217,6 +217,65 @@ def test_max_k_rotate_quant(cr):
     gu.assert_equal(_f32_bits(gu.host(sx)), _f32_bits(os_), "s_x max k")
 
 
+def _swiglu_pairs_input(m, i, seed):
+    """fc1-output-like bf16 gate/up rows [m, 2i] with special rows: an all-zero
+    up half (scale 0), gates below -88.72 (silu underflows to -0), large gates
+    (silu(g) = g), and mixed magnitudes elsewhere."""
+    rng = np.random.default_rng(seed)
+    g = rng.standard_normal((m, i)) * np.array([0.5, 4.0, 30.0])[rng.integers(0, 3, (m, i))]
+    u = rng.standard_normal((m, i)) * 3.0
+    if m > 0:
+        u[0] = 0.0
+    if m > 1:
+        g[1, ::3] = -200.0
+    if m > 2:
+        g[2] = 150.0 + rng.random(i)
+    return workloads.to_bf16_bits(np.concatenate([g, u], axis=1).astype(np.float32))
+
+
+@pytest.mark.parametrize("m,i", [(1, 256), (37, 768), (300, 5376), (64, 14336), (3, 33024), (2, 133120)])
+def test_swiglu_rotate_quant(cr, m, i):
+    """SwiGLU on fc1's bf16 output, then rotate + quantize per token: codes and
+    scales bit-exact against the oracle (row kernel for 1..32 groups per pass,
+    the recomputing kernel for 129 and 520 groups)."""
+    gu_in = _swiglu_pairs_input(m, i, seed=m + i)
+    qh, sh = cr.swiglu_rotate_quant_act(gu.dev_bf16(gu_in))
+    oq, os_ = oracle.swiglu_rotate_quant_act(gu_in)
+    gu.assert_equal(gu.host(qh), oq, "swiglu_rotate_quant q_h %dx%d" % (m, i))
+    gu.assert_equal(_f32_bits(gu.host(sh)), _f32_bits(os_), "swiglu_rotate_quant s_h %dx%d" % (m, i))
+    if m > 0:
+        assert gu.host(sh)[0] == 0 and not gu.host(qh)[0].any()
+
+
+def test_output_side_swiglu_chain_small(cr):
+    """The whole FFN with SwiGLU on fc1's output side, small: x -> fc1 (bf16
+    dequant on 2i columns) -> SwiGLU + rotate + quantize -> down GEMM, against
+    the oracle's composition of the same steps, bit for bit at every stage."""
+    import torch
+    rng = np.random.default_rng(41)
+    m, k, i, n = 200, 512, 768, 300
+    x = rng.laplace(size=(m, k)).astype(np.float32)
+    x[:, rng.choice(k, 5, replace=False)] *= 30
+    xb = workloads.to_bf16_bits(x)
+    w1 = (0.05 * rng.standard_normal((2 * i, k))).astype(np.float32)
+    w2 = (0.03 * rng.standard_normal((n, i))).astype(np.float32)
+    q1, s1 = cr.quantize_weight(gu.dev(w1))
+    q2, s2 = cr.quantize_weight(gu.dev(w2))
+    gu_d = cr.linear(gu.dev_bf16(xb), q1, s1)
+    qh, sh = cr.swiglu_rotate_quant_act(gu_d)
+    y = cr.gemm_dequant(qh, sh, q2, s2)
+    torch.cuda.synchronize()
+    oq1, os1 = oracle.quantize_weight(w1)
+    oq2, os2 = oracle.quantize_weight(w2)
+    ogu = oracle.linear_rows(xb, oq1, os1)
+    oqh, osh = oracle.swiglu_rotate_quant_act(ogu)
+    oy = oracle.dequant_bf16(oracle.gemm_s32(oqh, oq2), osh, os2)
+    gu.assert_bf16_parity(gu.host_bf16(gu_d), ogu, "output-side chain: fc1 gate/up")
+    gu.assert_equal(gu.host(qh), oqh, "output-side chain: q_h")
+    gu.assert_equal(_f32_bits(gu.host(sh)), _f32_bits(osh), "output-side chain: s_h")
+    gu.assert_bf16_parity(gu.host_bf16(y), oy, "output-side chain: y")
+
+
 def test_zero_size_calls(cr):
     import torch
     x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
