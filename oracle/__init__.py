@@ -74,6 +74,8 @@ def lib() -> ctypes.CDLL:
         L.orc_swiglu_pairs_bf16.argtypes = [P, I64, I64, P]
         L.orc_swiglu_rotate_quant_rows.argtypes = [P, I64, P, I64, P, P]
         L.orc_swiglu_rotate_quant_rows.restype = ctypes.c_int
+        L.orc_dequantize_weight.argtypes = [P, P, I64, I64, P]
+        L.orc_lora_add.argtypes = [P, I64, I64, P, P, I64, ctypes.c_float]
         _lib = L
     return _lib
 
@@ -262,6 +264,34 @@ def swiglu_rotate_quant_act(gu_bf16: np.ndarray, rows: np.ndarray | None = None)
     if rc != 0:
         raise ValueError("oracle swiglu_rotate_quant_act failed (i=%d)" % i)
     return q, s
+
+
+def dequantize_weight(q_w: np.ndarray, s_w: np.ndarray) -> np.ndarray:
+    """fp32 W [n, k] = (q . s) . H/16 per row: the unrotated weights."""
+    q_w = np.ascontiguousarray(q_w, dtype=np.int8)
+    s_w = np.ascontiguousarray(s_w, dtype=np.float32)
+    n, k = q_w.shape
+    assert s_w.size == n and k % 256 == 0
+    w = np.empty((n, k), np.float32)
+    lib().orc_dequantize_weight(_p(q_w), _p(s_w), n, k, _p(w))
+    return w
+
+
+def lora_add(w: np.ndarray, b: np.ndarray, a: np.ndarray, scale: float) -> np.ndarray:
+    """W + scale * (B . A) with the fp32 order of the definition (returns a copy)."""
+    w = np.array(w, dtype=np.float32, copy=True, order="C")
+    b = np.ascontiguousarray(b, dtype=np.float32)
+    a = np.ascontiguousarray(a, dtype=np.float32)
+    n, k = w.shape
+    rank = b.shape[1]
+    assert b.shape == (n, rank) and a.shape == (rank, k)
+    lib().orc_lora_add(_p(w), n, k, _p(b), _p(a), rank, float(scale))
+    return w
+
+
+def merge_lora(q_w, s_w, b, a, scale):
+    """Dequantize, add the low-rank delta, requantize: new (q_w, s_w)."""
+    return quantize_weight(lora_add(dequantize_weight(q_w, s_w), b, a, scale))
 
 
 # ------------------------------------------------------------------ compositions

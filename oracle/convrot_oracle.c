@@ -363,3 +363,43 @@ int orc_swiglu_rotate_quant_rows(const uint16_t* gu, int64_t i_width, const int6
     }
     return fail ? -1 : 0;
 }
+
+/* ----------------------------------------- weight dequantize / LoRA merge */
+
+/* Dequantize ConvRot weights back to the unrotated basis (h3-rs README, model
+ * file table: quantized weights are dequantized per layer by kernels; "Speed":
+ * LoRAs are merged at load by dequantizing, adding and requantizing).
+ * Reading: W = (q . s) . H/16 per row; since H/16 is its own inverse this
+ * undoes the rotation.  The codes are rotated first: with |q| <= 127 every
+ * butterfly partial sum is an integer below 2^15, so orc_fwht256 (butterfly
+ * then the exact 1/16) is exact, and the only rounding is the one multiply
+ * w = RN((H q / 16) * s). */
+void orc_dequantize_weight(const int8_t* q, const float* s, int64_t n, int64_t k, float* w) {
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < n; ++r) {
+        float* row = w + r * k;
+        for (int64_t c = 0; c < k; ++c) row[c] = (float)q[r * k + c];
+        orc_rotate_row(row, k);
+        for (int64_t c = 0; c < k; ++c) row[c] = row[c] * s[r];
+    }
+}
+
+/* Low-rank delta added in place: W[n][c] += scale * sum_j B[n][j] * A[j][c]
+ * (h3-rs README: ComfyUI LoRA files, merged at load; B is the up factor
+ * [n, rank], A the down factor [rank, k], scale the caller's strength times
+ * alpha / rank).  Reading of the fp32 arithmetic: the sum runs over j in
+ * increasing order as a chain of fused multiply-adds starting from 0, then
+ * one multiply by scale and one add to W. */
+void orc_lora_add(float* w, int64_t n, int64_t k, const float* b, const float* a, int64_t rank,
+                  float scale) {
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < n; ++r) {
+        for (int64_t c = 0; c < k; ++c) {
+            float acc = 0.0f;
+            for (int64_t j = 0; j < rank; ++j) acc = fmaf(b[r * rank + j], a[j * k + c], acc);
+            w[r * k + c] = w[r * k + c] + scale * acc;
+        }
+    }
+}

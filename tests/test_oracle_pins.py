@@ -624,3 +624,75 @@ def test_swiglu_rotate_quant_composes():
     rows = np.array([8, 3, 0])
     qr, sr = oracle.swiglu_rotate_quant_act(gu, rows)
     assert np.array_equal(qr, q[rows]) and np.array_equal(sr, s[rows])
+
+
+# ------------------------------------------------ weight dequantize / LoRA merge
+
+def test_dequantize_weight_closed_form():
+    """W = RN((H q / 16) * s) per 256-group, from the Sylvester matrix in exact
+    integer arithmetic and the scale applied in fp64 (exact: under 40 bits),
+    then one rounding to fp32: bit-equal to the oracle.  A wrong axis, sign,
+    group, normalization or row scale fails."""
+    rng = np.random.default_rng(51)
+    n, k = 12, 768
+    q = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    q[0] = 127                                 # extremes of the exact range
+    q[1] = -127
+    s = (rng.random(n) * 0.05 + 1e-4).astype(np.float32)
+    s[2] = np.float32(2.0 ** -20)
+    H = hd.H().astype(np.int64)
+    rot = np.concatenate([q[:, g * 256:(g + 1) * 256].astype(np.int64) @ H for g in range(k // 256)], axis=1)
+    ref = ((rot.astype(np.float64) / 16.0) * s[:, None].astype(np.float64)).astype(np.float32)
+    w = oracle.dequantize_weight(q, s)
+    assert np.array_equal(w.view(np.uint32), ref.view(np.uint32))
+
+
+def test_dequantize_requantize_round_trip():
+    """Quantizing dequantized weights returns the same codes (the rotation
+    back and forth moves each value by far less than half a code step) and
+    scales within 2 ulps; a merge with zero strength changes no code."""
+    rng = np.random.default_rng(52)
+    w = (0.02 * rng.standard_normal((40, 1024))).astype(np.float32)
+    w[:, rng.choice(1024, 8, replace=False)] *= 20
+    q, s = oracle.quantize_weight(w)
+    q2, s2 = oracle.quantize_weight(oracle.dequantize_weight(q, s))
+    assert np.array_equal(q, q2)
+    assert np.abs(s2.view(np.int32).astype(np.int64) - s.view(np.int32)).max() <= 2
+    b = rng.standard_normal((40, 8)).astype(np.float32)
+    a = rng.standard_normal((8, 1024)).astype(np.float32)
+    q3, _ = oracle.merge_lora(q, s, b, a, 0.0)
+    assert np.array_equal(q, q3)
+
+
+def test_lora_add_exact_on_integers():
+    """Small-integer factors and weights keep every fp32 step exact, so
+    W + scale (B . A) must equal numpy's int64 matmul exactly (B is [n, rank],
+    A is [rank, k]; a transposed or swapped operand fails)."""
+    rng = np.random.default_rng(53)
+    n, k, r = 20, 512, 16
+    b = rng.integers(-8, 9, size=(n, r))
+    a = rng.integers(-8, 9, size=(r, k))
+    w = rng.integers(-1000, 1001, size=(n, k))
+    for scale in (1.0, 0.5, -2.0):
+        got = oracle.lora_add(w.astype(np.float32), b.astype(np.float32), a.astype(np.float32), scale)
+        ref = w + scale * (b @ a)
+        assert np.array_equal(got, ref.astype(np.float32)), scale
+
+
+def test_lora_add_rounding_bound():
+    """Random fp32 factors: within the sequential fused-multiply-add summation
+    bound gamma_r * sum|b a| (scaled), plus one rounding each for the scale
+    multiply and the final add, of the fp64 value."""
+    rng = np.random.default_rng(54)
+    n, k, r = 16, 256, 64
+    b = rng.standard_normal((n, r)).astype(np.float32)
+    a = rng.standard_normal((r, k)).astype(np.float32)
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    scale = np.float32(0.37)
+    got = oracle.lora_add(w, b, a, scale).astype(np.float64)
+    d64 = b.astype(np.float64) @ a.astype(np.float64)
+    ref = w.astype(np.float64) + float(scale) * d64
+    gamma = r * U / (1 - r * U)
+    bound = (abs(float(scale)) * (gamma * (np.abs(b).astype(np.float64) @ np.abs(a).astype(np.float64))
+                                  + 2 * U * np.abs(d64)) + 2 * U * np.abs(ref))
+    assert np.all(np.abs(got - ref) <= bound)
