@@ -300,6 +300,28 @@ def main():
                 "rotates and quantizes it",
     }
 
+    # Load-time LoRA merge into the FFN-up weight (dequantize, add a rank-32
+    # delta, requantize), as it runs once per weight at load.
+    lr = 32
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    lb = torch.randn((N1, lr), device=dev, generator=g) * 0.02
+    la = torch.randn((lr, K1), device=dev, generator=g) * 0.02
+    mq = torch.empty_like(qwu)
+    ms_ = torch.empty_like(swu)
+    mws = torch.empty(4 * N1 * K1, dtype=torch.uint8, device=dev)
+    cr.merge_lora(qwu, swu, lb, la, 0.5, q_out=mq, s_out=ms_, workspace=mws)
+    torch.cuda.synchronize()
+    m0, m1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    m0.record()
+    for _ in range(5):
+        cr.merge_lora(qwu, swu, lb, la, 0.5, q_out=mq, s_out=ms_, workspace=mws)
+    m1.record()
+    torch.cuda.synchronize()
+    merge_ms = m0.elapsed_time(m1) / 5
+    merge_bytes = 18.0 * N1 * K1 + 4.0 * lr * (N1 + K1) + 8.0 * N1
+    del lb, la, mq, ms_, mws
+
     # cross-check: the same step through the fused entry points (same kernels)
     torch.cuda.synchronize()
     ws = torch.empty(max(cr.workspace_bytes(M, K1), cr.workspace_bytes(M, K2)), dtype=torch.uint8, device=dev)
@@ -344,6 +366,10 @@ def main():
         "fused_api_ms_per_step": round(fused_ms, 4),
         "output_side_swiglu": out_side,
         "weight_quant": {"ms": round(wq_ms, 4), "GB/s": round(wq_bytes / (wq_ms * 1e-3) / 1e9, 1)},
+        "lora_merge_ffn_up": {"ms": round(merge_ms, 4), "rank": lr,
+                              "GB/s": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1),
+                              "note": "dequantize + rank-32 delta + requantize of the 28672 x 5376 weight, "
+                                      "load time; algorithmic bytes 18 n k + 4 r (n + k) + 8 n"},
         "wall_s": round(wall, 3),
     }
     print(json.dumps(out), flush=True)

@@ -158,6 +158,43 @@ int convrot_gemm_swiglu(const int8_t* q_x, const float* s_x, const int8_t* q_w,
 int convrot_gemm_s32(const int8_t* q_x, const int8_t* q_w, int64_t m, int64_t n, int64_t k,
                      int32_t* acc, void* stream);
 
+/* ---- load-time weight operations: merging a LoRA into ConvRot weights ----
+ * (h3-rs README, "Speed": LoRAs are merged into the int8 weights at load by
+ * dequantizing, adding and requantizing, so they cost nothing per step;
+ * model file table: quantized weights are dequantized per layer by kernels.) */
+
+/* Dequantize ConvRot weights back to the unrotated basis:
+ *   w[r][c] = RN((H q_r / 16)[c] * s_w[r]) per 256-group (H/16 is its own
+ *   inverse; the code rotation is exact in fp32, the multiply is the only
+ *   rounding).
+ *   q_w [n, k] int8, s_w [n] fp32 (from convrot_quantize_weight); w [n, k] fp32
+ *   output.  Sizes as convrot_quantize_weight.                              */
+int convrot_dequantize_weight(const int8_t* q_w, const float* s_w, int64_t n, int64_t k,
+                              float* w, void* stream);
+
+/* Add a low-rank delta in place: w[r][c] += scale * sum_j b[r][j] * a[j][c],
+ * the sum over j in increasing order as a chain of fp32 fused multiply-adds
+ * from 0, then one multiply by scale and one add (each rounded to nearest).
+ *   w [n, k] fp32 (in/out); b [n, rank] fp32 (the LoRA up factor); a [rank, k]
+ *   fp32 (the down factor); scale = strength * alpha / rank, as the caller
+ *   defines it.  rank >= 0; b and a may be NULL when rank == 0.              */
+int convrot_lora_add(float* w, int64_t n, int64_t k, const float* lora_b, const float* lora_a,
+                     int64_t rank, float scale, void* stream);
+
+/* Workspace convrot_merge_lora needs: the fp32 weights, 4 * n * k bytes
+ * (0 for invalid sizes).                                                     */
+size_t convrot_merge_workspace_bytes(int64_t n, int64_t k);
+
+/* Merge a LoRA into ConvRot weights: dequantize (as convrot_dequantize_weight)
+ * into the workspace, add the delta there (as convrot_lora_add), and quantize
+ * the result again (as convrot_quantize_weight) into q_out / s_out.  The three
+ * steps run in order on the stream, so q_out / s_out may be q_w / s_w (an
+ * in-place update).  On return the workspace holds the merged fp32 weights. */
+int convrot_merge_lora(const int8_t* q_w, const float* s_w, int64_t n, int64_t k,
+                       const float* lora_b, const float* lora_a, int64_t rank, float scale,
+                       int8_t* q_out, float* s_out, void* workspace, size_t workspace_bytes,
+                       void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL).         */
 const char* convrot_status_string(int status);
 

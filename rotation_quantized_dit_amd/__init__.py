@@ -11,12 +11,15 @@ from ._lib import (  # noqa: F401
     GROUP,
     MAX_K,
     ConvRotError,
+    dequantize_weight,
     gemm_dequant,
     gemm_s32,
     gemm_swiglu,
     linear,
     linear_swiglu,
+    lora_add,
     load_library,
+    merge_lora,
     quantize_weight,
     rotate_quant_act,
     status_string,

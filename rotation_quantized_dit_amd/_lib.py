@@ -25,7 +25,8 @@ OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH = range(6)
 SYMBOLS = (
     "convrot_quantize_weight", "convrot_rotate_quant_act", "convrot_workspace_bytes",
     "convrot_linear", "convrot_linear_swiglu", "convrot_gemm_dequant", "convrot_gemm_swiglu",
-    "convrot_gemm_s32", "convrot_swiglu_rotate_quant_act", "convrot_status_string",
+    "convrot_gemm_s32", "convrot_swiglu_rotate_quant_act", "convrot_dequantize_weight",
+    "convrot_lora_add", "convrot_merge_workspace_bytes", "convrot_merge_lora", "convrot_status_string",
 )
 
 
@@ -60,6 +61,10 @@ def load_library() -> ctypes.CDLL:
             "convrot_gemm_dequant": ([P, P, P, P, I64, I64, I64, P, P], I),
             "convrot_gemm_swiglu": ([P, P, P, P, I64, I64, I64, P, P], I),
             "convrot_gemm_s32": ([P, P, I64, I64, I64, P, P], I),
+            "convrot_dequantize_weight": ([P, P, I64, I64, P, P], I),
+            "convrot_lora_add": ([P, I64, I64, P, P, I64, ctypes.c_float, P], I),
+            "convrot_merge_workspace_bytes": ([I64, I64], SZ),
+            "convrot_merge_lora": ([P, P, I64, I64, P, P, I64, ctypes.c_float, P, P, P, SZ, P], I),
             "convrot_status_string": ([I], ctypes.c_char_p),
         }
         for name, (args, res) in sig.items():
@@ -236,3 +241,59 @@ def gemm_s32(q_x, q_w, out=None):
     _check("convrot_gemm_s32", load_library().convrot_gemm_s32(
         q_x.data_ptr(), q_w.data_ptr(), m, n, k, acc.data_ptr(), _stream()))
     return acc
+
+
+# ------------------------------------------------------------------ load-time weight operations
+
+def dequantize_weight(q_w: torch.Tensor, s_w: torch.Tensor, out=None):
+    """int8 codes [n, k] + fp32 row scales [n] -> fp32 W [n, k] (unrotated)."""
+    _dev(q_w, "q_w", torch.int8, 2)
+    _dev(s_w, "s_w", torch.float32, 1)
+    n, k = q_w.shape
+    if s_w.shape[0] != n:
+        raise ValueError("s_w must have %d entries" % n)
+    w = _out(out, (n, k), torch.float32, q_w, "out")
+    _check("convrot_dequantize_weight", load_library().convrot_dequantize_weight(
+        q_w.data_ptr(), s_w.data_ptr(), n, k, w.data_ptr(), _stream()))
+    return w
+
+
+def _lora_args(n, k, b, a):
+    if b is None or a is None:
+        raise ValueError("lora_b and lora_a are required")
+    _dev(b, "lora_b", torch.float32, 2)
+    _dev(a, "lora_a", torch.float32, 2)
+    rank = b.shape[1]
+    if b.shape[0] != n or tuple(a.shape) != (rank, k):
+        raise ValueError("lora_b must be [%d, r] and lora_a [r, %d] (got %s, %s)"
+                         % (n, k, tuple(b.shape), tuple(a.shape)))
+    return rank
+
+
+def lora_add(w: torch.Tensor, lora_b: torch.Tensor, lora_a: torch.Tensor, scale: float):
+    """In place: w [n, k] += scale * (lora_b [n, r] . lora_a [r, k]); returns w."""
+    _dev(w, "w", torch.float32, 2)
+    n, k = w.shape
+    rank = _lora_args(n, k, lora_b, lora_a)
+    _check("convrot_lora_add", load_library().convrot_lora_add(
+        w.data_ptr(), n, k, lora_b.data_ptr(), lora_a.data_ptr(), rank, float(scale), _stream()))
+    return w
+
+
+def merge_lora(q_w: torch.Tensor, s_w: torch.Tensor, lora_b: torch.Tensor, lora_a: torch.Tensor,
+               scale: float, q_out=None, s_out=None, workspace=None):
+    """Dequantize, add scale * (lora_b . lora_a), requantize: new (q_w, s_w).
+    Pass q_out=q_w, s_out=s_w to update in place."""
+    _dev(q_w, "q_w", torch.int8, 2)
+    _dev(s_w, "s_w", torch.float32, 1)
+    n, k = q_w.shape
+    rank = _lora_args(n, k, lora_b, lora_a)
+    q_out = _out(q_out, (n, k), torch.int8, q_w, "q_out")
+    s_out = _out(s_out, (n,), torch.float32, q_w, "s_out")
+    need = int(load_library().convrot_merge_workspace_bytes(n, k))
+    if workspace is None:
+        workspace = torch.empty(max(need, 16), dtype=torch.uint8, device=q_w.device)
+    _check("convrot_merge_lora", load_library().convrot_merge_lora(
+        q_w.data_ptr(), s_w.data_ptr(), n, k, lora_b.data_ptr(), lora_a.data_ptr(), rank, float(scale),
+        q_out.data_ptr(), s_out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()))
+    return q_out, s_out

@@ -107,6 +107,64 @@ int convrot_swiglu_rotate_quant_act(const uint16_t* gu, int64_t m, int64_t i, in
     return launched(convrot::launch_swiglu_rotate_quant(gu, m, i, q_h, s_h, (hipStream_t)stream));
 }
 
+// Load-time weight operations.  Their grids are 1-D: at most 2^31 - 1
+// workgroups of 16 groups (dequantize) or of 1024 columns x 8 rows (LoRA).
+static int check_weight_grid(int64_t n, int64_t k) {
+    const int64_t groups = n * (k / 256);
+    if ((groups + 15) / 16 > (int64_t)INT32_MAX) return CONVROT_ERR_SHAPE;
+    if (((k / 4 + 255) / 256) * ((n + 7) / 8) > (int64_t)INT32_MAX) return CONVROT_ERR_SHAPE;
+    return CONVROT_OK;
+}
+
+int convrot_dequantize_weight(const int8_t* q_w, const float* s_w, int64_t n, int64_t k, float* w,
+                              void* stream) {
+    int st;
+    if ((st = check_rows(n)) || (st = check_k(k)) || (st = check_weight_grid(n, k))) return st;
+    if (n == 0) return CONVROT_OK;
+    if (!q_w || !s_w || !w) return CONVROT_ERR_NULL;
+    if (!aligned16(q_w) || !aligned16(s_w) || !aligned16(w)) return CONVROT_ERR_ALIGN;
+    return launched(convrot::launch_dequantize_weight(q_w, s_w, n, k, w, (hipStream_t)stream));
+}
+
+int convrot_lora_add(float* w, int64_t n, int64_t k, const float* lora_b, const float* lora_a,
+                     int64_t rank, float scale, void* stream) {
+    int st;
+    if ((st = check_rows(n)) || (st = check_k(k)) || (st = check_rows(rank)) ||
+        (st = check_weight_grid(n, k)))
+        return st;
+    if (n == 0) return CONVROT_OK;
+    if (!w || (rank > 0 && (!lora_b || !lora_a))) return CONVROT_ERR_NULL;
+    if (!aligned16(w) || !aligned16(lora_b) || !aligned16(lora_a)) return CONVROT_ERR_ALIGN;
+    return launched(convrot::launch_lora_add(w, n, k, lora_b, lora_a, rank, scale, (hipStream_t)stream));
+}
+
+size_t convrot_merge_workspace_bytes(int64_t n, int64_t k) {
+    if (check_rows(n) || check_k(k)) return 0;
+    return 4u * (size_t)n * (size_t)k;
+}
+
+int convrot_merge_lora(const int8_t* q_w, const float* s_w, int64_t n, int64_t k, const float* lora_b,
+                       const float* lora_a, int64_t rank, float scale, int8_t* q_out, float* s_out,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    int st;
+    if ((st = check_rows(n)) || (st = check_k(k)) || (st = check_rows(rank)) ||
+        (st = check_weight_grid(n, k)))
+        return st;
+    if (n == 0) return CONVROT_OK;
+    if (!q_w || !s_w || !q_out || !s_out || (rank > 0 && (!lora_b || !lora_a))) return CONVROT_ERR_NULL;
+    if (!aligned16(q_w) || !aligned16(s_w) || !aligned16(q_out) || !aligned16(s_out) ||
+        !aligned16(lora_b) || !aligned16(lora_a))
+        return CONVROT_ERR_ALIGN;
+    if (!workspace || workspace_bytes < convrot_merge_workspace_bytes(n, k)) return CONVROT_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return CONVROT_ERR_ALIGN;
+    float* w = (float*)workspace;
+    hipStream_t s = (hipStream_t)stream;
+    if (convrot::launch_dequantize_weight(q_w, s_w, n, k, w, s) != hipSuccess) return CONVROT_ERR_LAUNCH;
+    if (convrot::launch_lora_add(w, n, k, lora_b, lora_a, rank, scale, s) != hipSuccess)
+        return CONVROT_ERR_LAUNCH;
+    return launched(convrot::launch_rotate_quant_f32(w, n, k, q_out, s_out, s));
+}
+
 int convrot_gemm_s32(const int8_t* q_x, const int8_t* q_w, int64_t m, int64_t n, int64_t k,
                      int32_t* acc, void* stream) {
     int st = check_gemm_shape(m, n, n, k);

@@ -17,6 +17,13 @@ hipError_t launch_rotate_quant_f32(const float* x, int64_t rows, int64_t k, int8
 hipError_t launch_swiglu_rotate_quant(const uint16_t* gu, int64_t rows, int64_t i, int8_t* q,
                                       float* s, hipStream_t stream);
 
+// Load-time weight operations: W = (q . s) . H/16 per row, and
+// W += scale * (B . A) in place (b [n, rank], a [rank, k]).
+hipError_t launch_dequantize_weight(const int8_t* q, const float* s, int64_t n, int64_t k,
+                                    float* w, hipStream_t stream);
+hipError_t launch_lora_add(float* w, int64_t n, int64_t k, const float* b, const float* a,
+                           int64_t rank, float scale, hipStream_t stream);
+
 // K-GEMM: int8 x int8 -> int32 on MFMA with one of three epilogues.
 enum class Epilogue { S32, BF16, SWIGLU };
 

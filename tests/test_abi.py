@@ -161,3 +161,27 @@ def test_python_binding_rejects_cpu_tensors():
         cr.rotate_quant_act(torch.zeros(4, 256, dtype=torch.bfloat16))
     with pytest.raises((TypeError, ValueError)):
         cr.quantize_weight(torch.zeros(4, 256, dtype=torch.float64))
+
+
+def test_weight_ops_validation(L):
+    """Load-time weight entry points: host-side checks before any launch."""
+    from rotation_quantized_dit_amd._lib import ERR_ALIGN, ERR_NULL, ERR_SHAPE, ERR_WORKSPACE, OK
+    assert L.convrot_dequantize_weight(A, B, 4, 300, C, None) == ERR_SHAPE
+    assert L.convrot_dequantize_weight(A, B, -1, 256, C, None) == ERR_SHAPE
+    assert L.convrot_dequantize_weight(None, B, 4, 256, C, None) == ERR_NULL
+    assert L.convrot_dequantize_weight(A, B, 4, 256, C + 4, None) == ERR_ALIGN
+    assert L.convrot_dequantize_weight(None, None, 0, 256, None, None) == OK
+    assert L.convrot_lora_add(A, 4, 256, B, C, -1, 1.0, None) == ERR_SHAPE
+    assert L.convrot_lora_add(A, 4, 512, None, C, 3, 1.0, None) == ERR_NULL
+    assert L.convrot_lora_add(A, 4, 512, B, None, 3, 1.0, None) == ERR_NULL
+    assert L.convrot_lora_add(A, 4, 512, B + 4, C, 3, 1.0, None) == ERR_ALIGN
+    assert L.convrot_lora_add(A, 0, 512, None, None, 3, 1.0, None) == OK
+    assert L.convrot_merge_workspace_bytes(10, 512) == 4 * 10 * 512
+    assert L.convrot_merge_workspace_bytes(10, 500) == 0
+    need = L.convrot_merge_workspace_bytes(4, 256)
+    assert L.convrot_merge_lora(A, B, 4, 256, C, D, 2, 1.0, A, B, D, need - 1, None) == ERR_WORKSPACE
+    assert L.convrot_merge_lora(A, B, 4, 256, C, D, 2, 1.0, A, B, None, need, None) == ERR_WORKSPACE
+    assert L.convrot_merge_lora(A, B, 4, 256, C, D, 2, 1.0, A, B, MIS, need, None) == ERR_ALIGN
+    assert L.convrot_merge_lora(A, None, 4, 256, C, D, 2, 1.0, A, B, D, need, None) == ERR_NULL
+    assert L.convrot_merge_lora(A, B, 4, 257, C, D, 2, 1.0, A, B, D, need, None) == ERR_SHAPE
+    assert L.convrot_merge_lora(None, None, 0, 256, None, None, 2, 1.0, None, None, None, 0, None) == OK

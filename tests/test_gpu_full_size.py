@@ -227,3 +227,28 @@ def test_block_chain_finite_and_tail_rows(block_chain):
     g, _, rows = block_chain
     assert g["finite"]
     assert np.any(rows >= workloads.VIDEO_TOKENS) and rows.max() == 32463
+
+
+# ------------------------------------------------------------------ load-time LoRA merge
+
+def test_merge_lora_ffn_up_weight_all_rows(cr):
+    """A rank-32 LoRA merged into the FFN-up weight (28672 x 5376) at load:
+    dequantize, add, requantize; every code and scale bit-exact against the
+    oracle."""
+    import torch
+    c = workloads.WORKLOADS["ffn_up"]
+    rng = np.random.default_rng(71)
+    print("merge_lora: drawing the ffn_up weight and a rank-32 delta", flush=True)
+    w = (0.02 * rng.standard_normal((c.n, c.k), dtype=np.float32)).astype(np.float32)
+    b = (0.02 * rng.standard_normal((c.n, 32), dtype=np.float32)).astype(np.float32)
+    a = (0.02 * rng.standard_normal((32, c.k), dtype=np.float32)).astype(np.float32)
+    qd, sd = cr.quantize_weight(gu.dev(w))
+    q2, s2 = cr.merge_lora(qd, sd, gu.dev(b), gu.dev(a), 0.5)
+    torch.cuda.synchronize()
+    gq, gs = gu.host(q2), gu.host(s2)
+    del qd, sd, q2, s2
+    print("merge_lora: oracle", flush=True)
+    oq, os_ = oracle.quantize_weight(w)
+    mq, ms = oracle.merge_lora(oq, os_, b, a, 0.5)
+    gu.assert_equal(gq, mq, "merged ffn_up codes (all rows)")
+    gu.assert_equal(_f32_bits(gs), _f32_bits(ms), "merged ffn_up scales (all rows)")

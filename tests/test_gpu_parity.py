@@ -276,6 +276,56 @@ def test_output_side_swiglu_chain_small(cr):
     gu.assert_bf16_parity(gu.host_bf16(y), oy, "output-side chain: y")
 
 
+@pytest.mark.parametrize("n,k", [(1, 256), (37, 768), (100, 5376), (3, 133120)])
+def test_dequantize_weight(cr, n, k):
+    """W = RN((H q / 16) * s): bit-exact against the oracle, codes at +-127
+    included, on ragged row counts and up to the largest k."""
+    rng = np.random.default_rng(n + k)
+    q = rng.integers(-127, 128, size=(n, k), dtype=np.int8)
+    q[0, :256] = 127
+    s = (rng.random(n) * 0.05 + 1e-5).astype(np.float32)
+    w = cr.dequantize_weight(gu.dev(q), gu.dev(s))
+    gu.assert_equal(_f32_bits(gu.host(w)), _f32_bits(oracle.dequantize_weight(q, s)),
+                    "dequantize_weight %dx%d" % (n, k))
+
+
+@pytest.mark.parametrize("n,k,r", [(5, 256, 0), (9, 512, 1), (37, 768, 7), (100, 1024, 64)])
+def test_lora_add(cr, n, k, r):
+    """W += scale * (B . A) with the fp32 order of the definition: bit-exact
+    against the oracle (rank 0 included; rows not a multiple of 8)."""
+    rng = np.random.default_rng(n * 3 + k + r)
+    w = rng.standard_normal((n, k)).astype(np.float32)
+    b = rng.standard_normal((n, max(r, 1))).astype(np.float32)[:, :r].copy()
+    a = rng.standard_normal((max(r, 1), k)).astype(np.float32)[:r].copy()
+    wd = gu.dev(w)
+    cr.lora_add(wd, gu.dev(b), gu.dev(a), 0.37)
+    gu.assert_equal(_f32_bits(gu.host(wd)), _f32_bits(oracle.lora_add(w, b, a, 0.37)),
+                    "lora_add %dx%d rank %d" % (n, k, r))
+
+
+def test_merge_lora_and_in_place(cr):
+    """Dequantize + LoRA add + requantize: codes and scales bit-exact against
+    the oracle, into fresh buffers and in place; zero strength keeps the codes."""
+    import torch
+    rng = np.random.default_rng(61)
+    n, k, r = 300, 1536, 16
+    w = (0.02 * rng.standard_normal((n, k))).astype(np.float32)
+    b = (0.01 * rng.standard_normal((n, r))).astype(np.float32)
+    a = (0.01 * rng.standard_normal((r, k))).astype(np.float32)
+    oq, os_ = oracle.quantize_weight(w)
+    mq, ms = oracle.merge_lora(oq, os_, b, a, 0.75)
+    qd, sd = gu.dev(oq), gu.dev(os_)
+    q2, s2 = cr.merge_lora(qd, sd, gu.dev(b), gu.dev(a), 0.75)
+    gu.assert_equal(gu.host(q2), mq, "merge_lora q")
+    gu.assert_equal(_f32_bits(gu.host(s2)), _f32_bits(ms), "merge_lora s")
+    cr.merge_lora(qd, sd, gu.dev(b), gu.dev(a), 0.75, q_out=qd, s_out=sd)
+    torch.cuda.synchronize()
+    gu.assert_equal(gu.host(qd), mq, "merge_lora in place q")
+    gu.assert_equal(_f32_bits(gu.host(sd)), _f32_bits(ms), "merge_lora in place s")
+    q0, _ = cr.merge_lora(gu.dev(oq), gu.dev(os_), gu.dev(b), gu.dev(a), 0.0)
+    gu.assert_equal(gu.host(q0), oq, "merge_lora zero strength")
+
+
 def test_zero_size_calls(cr):
     import torch
     x = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
