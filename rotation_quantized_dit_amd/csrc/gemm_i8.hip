@@ -12,14 +12,14 @@
 //            [0, i) are the gate, [i, 2i) the up projection);
 //            y[m][j] = bf16_rne(silu(g) * u), silu(g) = g / (1 + exp(-g)).
 //
-// Tiling.  A workgroup of 8 waves (two per SIMD) owns a 256 x 256 tile of acc
-// (for SwiGLU: 256 tokens x 128 gate columns + the matching 128 up columns).
-// Waves form a 4 (rows) x 2 (columns) grid; each owns 64 x 128 as 2 x 4
-// blocks of v_mfma_i32_32x32x32_i8 (32 x 32 outputs, 32 bytes of K per
-// instruction, 16 int32 accumulators per lane per block, 128 per lane in
-// all).  For SwiGLU a wave's 128 columns are 64 gate columns and the 64 up
-// columns of the same outputs, so every lane holds g and u of its elements.
-// K advances 64 bytes per stage through a 4-stage LDS ring (32 KiB per stage).
+// Tiling.  A workgroup of 8 waves (two per SIMD) owns a BM x 256 tile of acc
+// (BM tokens; for SwiGLU 128 gate columns + the matching 128 up columns).
+// Waves form a 4 (rows) x 2 (columns) grid; each owns 32 MA x 128 (MA =
+// BM / 128) as MA x 4 blocks of v_mfma_i32_32x32x32_i8 (32 x 32 outputs,
+// 32 bytes of K per instruction, 16 int32 accumulators per lane per block).
+// For SwiGLU a wave's 128 columns are 64 gate columns and the 64 up columns of
+// the same outputs, so every lane holds g and u of its elements.  K advances
+// 64 bytes per stage through an LDS ring of STAGES slots.
 //
 // Why two waves per SIMD: each SIMD issues at most one instruction per wave
 // every few cycles, and the fragment reads, the ring refills and their
@@ -54,24 +54,36 @@
 namespace convrot {
 namespace {
 
-constexpr int BM = 256;
-constexpr int BN = 256;
+#ifndef CONVROT_GEMM_BM
+#define CONVROT_GEMM_BM 384
+#endif
+constexpr int BM = CONVROT_GEMM_BM;   // tile rows (tokens): 4 wave rows x 32 MA
+constexpr int BN = 256;               // tile columns (weight rows)
 constexpr int BK = 64;
-constexpr int STAGES = 4;
+constexpr int MA = BM / 128;          // 32-row A blocks per wave
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int A_STAGE = BM * BK;
 constexpr int B_STAGE = BN * BK;
 constexpr int STAGE_BYTES = A_STAGE + B_STAGE;
-constexpr int RING_BYTES = STAGES * STAGE_BYTES;
-constexpr int GROUP_M = 8;
+// copies per wave per stage: MA of A (16 rows each) and 2 of B
+constexpr int COPIES = MA + 2;
 // Epilogue staging: each wave parks 32 rows x 128 int32 at a time, rows
 // padded to PITCH int32 to spread banks; it reuses the ring's memory.
 constexpr int PITCH = 136;
 constexpr int STASH_WAVE_BYTES = 32 * PITCH * 4;
-constexpr int LDS_BYTES = RING_BYTES > NWAVES * STASH_WAVE_BYTES ? RING_BYTES : NWAVES * STASH_WAVE_BYTES;
-// copies per wave per stage: A rows [32 w, 32 w + 32) and B rows [32 w, 32 w + 32)
-constexpr int COPIES = 4;
+constexpr int STASH_BYTES = NWAVES * STASH_WAVE_BYTES;
+// as many ring stages (at most 4) as fit in 160 KiB of LDS with the stash
+// (which reuses the ring) and the tile's scales
+constexpr int lds_for(int stages) {
+    return (stages * STAGE_BYTES > STASH_BYTES ? stages * STAGE_BYTES : STASH_BYTES) + 4 * (BM + BN);
+}
+constexpr int STAGES = lds_for(4) <= 160 * 1024 ? 4 : 3;
+constexpr int RING_BYTES = STAGES * STAGE_BYTES;
+constexpr int LDS_BYTES = RING_BYTES > STASH_BYTES ? RING_BYTES : STASH_BYTES;
+constexpr int GROUP_M = 8;
+static_assert(BM % 128 == 0 && MA >= 2 && MA <= 3, "tile rows");
+static_assert(LDS_BYTES + 4 * (BM + BN) <= 160 * 1024, "LDS budget");
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -146,40 +158,45 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     const float* __restrict__ sw, int M, int N, int K, void* __restrict__ out, int MT, int NT) {
     __shared__ __attribute__((aligned(1024))) int8_t lds[LDS_BYTES];
     __shared__ float sx_lds[BM];
+    __shared__ float sw_lds[BN];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int wm = wave >> 1;   // 64-row band of the tile
+    const int wm = wave >> 1;   // band of 32 MA rows of the tile
     const int wn = wave & 1;    // column half of the tile
     const Tile tile = map_tile(blockIdx.x, MT, NT);
     const int m0 = tile.tm * BM;
     const int rows_a = (M - m0) < BM ? (M - m0) : BM;
 
-    // Epilogue scales, loaded before the main loop so their latency is hidden:
-    // s_x of the tile's 256 rows (into LDS, read back per output row) and s_w
-    // of the lane's 8 output columns (gate and up columns for SwiGLU).
+    // Epilogue scales go to LDS before the main loop (their loads complete
+    // under it): s_x of the tile's rows, and s_w of its 256 weight rows (for
+    // SwiGLU the 128 gate rows, then the matching 128 up rows).
     constexpr int EPI_CG = EP == Epilogue::SWIGLU ? 8 : 16;   // column groups per wave row
     const int epi_cg = lane % EPI_CG;
     const int epi_ro = lane / EPI_CG;
     const int epi_col0 = EP == Epilogue::SWIGLU ? tile.tn * (BN / 2) + 64 * wn + 8 * epi_cg
                                                 : tile.tn * BN + 128 * wn + 8 * epi_cg;
-    float swa[8], swb[8];
     if constexpr (EP != Epilogue::S32) {
-        if (tid < BM) sx_lds[tid] = sx[tid < rows_a ? m0 + tid : M - 1];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int c = (epi_col0 + e) < N ? (epi_col0 + e) : (N - 1);
-            swa[e] = sw[c];
-            swb[e] = EP == Epilogue::SWIGLU ? sw[N + c] : 0.0f;
+        for (int r = tid; r < BM; r += NTHREADS) sx_lds[r] = sx[r < rows_a ? m0 + r : M - 1];
+        if (tid < BN) {
+            int c;
+            if constexpr (EP == Epilogue::SWIGLU) {
+                const int j = tile.tn * (BN / 2) + (tid & 127);
+                c = (j < N ? j : N - 1) + (tid < 128 ? 0 : N);
+            } else {
+                const int j = tile.tn * BN + tid;
+                c = j < N ? j : N - 1;
+            }
+            sw_lds[tid] = sw[c];
         }
     }
 
-    // Copy sources.  Copy i of wave w fills LDS rows 32 w + 16 i .. +15 of the
-    // A slab (i = 0, 1) or of the B slab (i = 2, 3) of a stage; lane l writes
-    // row (l / 4) of that group at chunk position l % 4, which holds logical
-    // chunk (l % 4) ^ swz(row).  Offsets are relative to a per-panel buffer
-    // resource (the tile's A rows; its gate rows; its up rows).
+    // Copy sources.  Copy i < MA of wave w fills A slab rows 16 (MA w + i) ..
+    // +15 of a stage; copy MA + i (i = 0, 1) fills B slab rows 32 w + 16 i ..
+    // +15.  Lane l writes row (l / 4) of its 16 at chunk position l % 4,
+    // which holds logical chunk (l % 4) ^ swz(row).  Offsets are relative to a
+    // per-panel buffer resource (the tile's A rows; its gate rows; its up rows).
     int b_first;   // first weight row of this tile (gate rows for SwiGLU)
     if constexpr (EP == Epilogue::SWIGLU)
         b_first = tile.tn * (BN / 2);
@@ -199,10 +216,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     uint32_t voff[COPIES];
 #pragma unroll
     for (int i = 0; i < COPIES; ++i) {
-        const int rr = 32 * wave + 16 * (i & 1) + (lane >> 2);   // row within the slab
+        const int rr = i < MA ? 16 * (MA * wave + i) + (lane >> 2)           // A slab row
+                              : 32 * wave + 16 * (i - MA) + (lane >> 2);    // B slab row
         const int c = (lane & 3) ^ swz(rr);
         int src_row;
-        if (i < 2) {
+        if (i < MA) {
             src_row = rr < rows_a ? rr : rows_a - 1;
         } else if constexpr (EP == Epilogue::SWIGLU) {
             const int j = rr & 127;   // the gate or up row of output column b_first + j
@@ -213,20 +231,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         voff[i] = (uint32_t)src_row * (uint32_t)K + 16u * (uint32_t)c;
     }
     auto issue = [&](int kt, int slot) {
-        int8_t* a_dst = lds + slot * STAGE_BYTES + 32 * 64 * wave;
-        int8_t* b_dst = a_dst + A_STAGE;
+        int8_t* a_dst = lds + slot * STAGE_BYTES + 16 * 64 * MA * wave;
+        int8_t* b_dst = lds + slot * STAGE_BYTES + A_STAGE + 32 * 64 * wave;
         const uint32_t soff = (uint32_t)kt * BK;
-        copy16(rsrc_a, a_dst, voff[0], soff);
-        copy16(rsrc_a, a_dst + 1024, voff[1], soff);
-        copy16(rsrc_b, b_dst, voff[2], soff);
-        copy16(rsrc_b, b_dst + 1024, voff[3], soff);
+#pragma unroll
+        for (int i = 0; i < MA; ++i) copy16(rsrc_a, a_dst + 1024 * i, voff[i], soff);
+        copy16(rsrc_b, b_dst, voff[MA], soff);
+        copy16(rsrc_b, b_dst + 1024, voff[MA + 1], soff);
     };
 
-    // LDS rows of this lane's fragments: A blocks a = 0, 1 (rows of the
-    // wave's band), B blocks b = 0..3 (for SwiGLU: b = 0, 1 gate, 2, 3 up).
-    int a_row[2], b_row[4];
+    // LDS rows of this lane's fragments: A blocks a < MA (rows of the wave's
+    // band), B blocks b = 0..3 (for SwiGLU: b = 0, 1 gate, 2, 3 up).
+    int a_row[MA], b_row[4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a) a_row[a] = 64 * wm + 32 * a + (lane & 31);
+    for (int a = 0; a < MA; ++a) a_row[a] = 32 * MA * wm + 32 * a + (lane & 31);
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
         if constexpr (EP == Epilogue::SWIGLU)
@@ -235,9 +253,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
             b_row[b] = 128 * wn + 32 * b + (lane & 31);
     }
 
-    v16i acc[2][4];
+    v16i acc[MA][4];
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int a = 0; a < MA; ++a)
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
@@ -245,24 +263,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
 
     // Byte offsets (within a stage) of this lane's 16-byte fragment reads for
     // the two 32-byte k-steps of a stage.
-    int a_off[2][2], b_off[2][4];
+    int a_off[2][MA], b_off[2][4];
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
         const int c = 2 * s + (lane >> 5);
 #pragma unroll
-        for (int a = 0; a < 2; ++a) a_off[s][a] = a_row[a] * BK + 16 * (c ^ swz(a_row[a]));
+        for (int a = 0; a < MA; ++a) a_off[s][a] = a_row[a] * BK + 16 * (c ^ swz(a_row[a]));
 #pragma unroll
         for (int b = 0; b < 4; ++b) b_off[s][b] = A_STAGE + b_row[b] * BK + 16 * (c ^ swz(b_row[b]));
     }
-    auto read_frags = [&](const int8_t* st, int s, v4i (&af)[2], v4i (&bf)[4]) {
+    auto read_frags = [&](const int8_t* st, int s, v4i (&af)[MA], v4i (&bf)[4]) {
 #pragma unroll
-        for (int a = 0; a < 2; ++a) af[a] = *reinterpret_cast<const v4i*>(st + a_off[s][a]);
+        for (int a = 0; a < MA; ++a) af[a] = *reinterpret_cast<const v4i*>(st + a_off[s][a]);
 #pragma unroll
         for (int b = 0; b < 4; ++b) bf[b] = *reinterpret_cast<const v4i*>(st + b_off[s][b]);
     };
-    auto mma = [&](const v4i (&af)[2], const v4i (&bf)[4]) {
+    auto mma = [&](const v4i (&af)[MA], const v4i (&bf)[4]) {
 #pragma unroll
-        for (int a = 0; a < 2; ++a)
+        for (int a = 0; a < MA; ++a)
 #pragma unroll
             for (int b = 0; b < 4; ++b)
                 acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], acc[a][b], 0, 0, 0);
@@ -276,84 +294,124 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     //   k-step 1: MFMAs on set 1, interleaved with the refill of stage kt's
     //             slot with stage kt + STAGES and the reads of stage kt + 1's
     //             k-step 0 into set 0.
-    // The steady-state loop runs while a refill remains (vmcnt: two later
-    // stages, COPIES copies each, may stay in flight); the last stages are
-    // peeled so that the loop body is straight-line code.
+    // At stage kt's barrier the stages after kt + 1 may stay in flight
+    // (STAGES - 2 of them, COPIES copies each).  The steady-state loop runs
+    // while a refill remains; the last stages are peeled so that the loop
+    // body is straight-line code.  K % 256 == 0, so KT >= 4 >= STAGES.
+    constexpr int NREAD = MA + 4;        // fragment reads per k-step
+    constexpr int NMFMA = 4 * MA;        // MFMAs per k-step
     const int KT = K / BK;
 #pragma unroll
-    for (int st = 0; st < STAGES; ++st)
-        if (st < KT) issue(st, st);
-    {
-        const int ahead = (KT - 1) < (STAGES - 1) ? (KT - 1) : (STAGES - 1);
-        if (ahead >= 3) wait_vmcnt<3 * COPIES>();
-        else if (ahead == 2) wait_vmcnt<2 * COPIES>();
-        else if (ahead == 1) wait_vmcnt<COPIES>();
-        else wait_vmcnt<0>();
-    }
+    for (int st = 0; st < STAGES; ++st) issue(st, st);
+    wait_vmcnt<(STAGES - 1) * COPIES>();
     lds_barrier();
-    v4i fa0[2], fb0[4], fa1[2], fb1[4];
-    read_frags(lds, 0, fa0, fb0);
 
     int kt = 0;
+    int slot = 0;                        // slot of stage kt
+    if constexpr (MA == 3) {
+        // 192 accumulators leave room for one fragment set only: each k-step
+        // reads its fragments and then issues its MFMAs (the other wave of the
+        // SIMD fills the read latency); the barrier sits between the k-steps,
+        // after the last reads of stage kt, and the refill of its slot is
+        // interleaved with the second k-step's MFMAs.
+        v4i fa[MA], fb[4];
+        for (; kt < KT; ++kt) {
+            const int next = slot + 1 == STAGES ? 0 : slot + 1;
+            const bool refill = kt + STAGES < KT;
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(lds + slot * STAGE_BYTES, 0, fa, fb);
+            mma(fa, fb);
+            __builtin_amdgcn_sched_barrier(0);
+            read_frags(lds + slot * STAGE_BYTES, 1, fa, fb);
+            // stage kt + 1 must have landed before the next iteration reads it
+            const int after = KT - 2 - kt;   // stages behind kt + 1 in flight (<= STAGES - 2)
+            if (after >= 1) wait_vmcnt<COPIES>();
+            else wait_vmcnt<0>();
+            lds_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+            if (refill) issue(kt + STAGES, slot);
+            mma(fa, fb);
+            __builtin_amdgcn_sched_barrier(0);
+            slot = next;
+        }
+    } else {
+    v4i fa0[MA], fb0[4], fa1[MA], fb1[4];
+    read_frags(lds, 0, fa0, fb0);
     for (; kt + STAGES < KT; ++kt) {
-        const int slot = kt & (STAGES - 1);
+        const int next = slot + 1 == STAGES ? 0 : slot + 1;
         __builtin_amdgcn_sched_barrier(0);
         read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1);
         mma(fa0, fb0);
 #pragma unroll
-        for (int i = 0; i < 6; ++i) {
+        for (int i = 0; i < NREAD; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<2 * COPIES>();
+        wait_vmcnt<(STAGES - 2) * COPIES>();
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(lds + ((kt + 1) & (STAGES - 1)) * STAGE_BYTES, 0, fa0, fb0);
+        read_frags(lds + next * STAGE_BYTES, 0, fa0, fb0);
         issue(kt + STAGES, slot);
         mma(fa1, fb1);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < COPIES; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
             __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one direct copy
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
+        for (int i = COPIES; i < NREAD; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
         __builtin_amdgcn_sched_barrier(0);
+        slot = next;
     }
-    // Peeled tail: at most STAGES - 1 stages with a successor, then the last.
+    // Peeled tail: the stages with a successor, then the last.
     for (; kt + 1 < KT; ++kt) {
-        const int slot = kt & (STAGES - 1);
+        const int next = slot + 1 == STAGES ? 0 : slot + 1;
         read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1);
         mma(fa0, fb0);
-        const int after = KT - 2 - kt;   // stages behind kt + 1 still in flight
-        if (after >= 2) wait_vmcnt<2 * COPIES>();
-        else if (after == 1) wait_vmcnt<COPIES>();
+        const int after = KT - 2 - kt;   // stages behind kt + 1 still in flight (<= STAGES - 2)
+        if (STAGES >= 4 && after >= 2) wait_vmcnt<2 * COPIES>();
+        else if (after >= 1) wait_vmcnt<COPIES>();
         else wait_vmcnt<0>();
         lds_barrier();
-        read_frags(lds + ((kt + 1) & (STAGES - 1)) * STAGE_BYTES, 0, fa0, fb0);
+        read_frags(lds + next * STAGE_BYTES, 0, fa0, fb0);
         mma(fa1, fb1);
+        slot = next;
     }
-    read_frags(lds + (kt & (STAGES - 1)) * STAGE_BYTES, 1, fa1, fb1);
+    read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1);
     mma(fa0, fb0);
     mma(fa1, fb1);
+    }
 
     // Epilogue.  Block (a, b), lane l, register r of the MFMA accumulators
     // holds row 32 a + 8 (r / 4) + 4 (l / 32) + r % 4 and column 32 b + l % 32
-    // of the wave's 64 x 128 sub-tile.  Row block by row block, each wave
+    // of the wave's 32 MA x 128 sub-tile.  Row block by row block, each wave
     // parks its 32 x 128 int32 accumulators in its own part of the (now free)
     // ring, then reads them back row-contiguous: every lane takes 8
     // consecutive columns of one row, applies the scales and the epilogue math
     // in a compact loop, and writes one 16-byte store.
     lds_barrier();   // every wave is done reading the ring
     int32_t* stash = reinterpret_cast<int32_t*>(lds + wave * STASH_WAVE_BYTES);
-    const int grow0 = m0 + 64 * wm;
+    const int grow0 = m0 + 32 * MA * wm;
+    float swa[8], swb[8];   // the lane's column scales (gate and up for SwiGLU)
+    if constexpr (EP != Epilogue::S32) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            if constexpr (EP == Epilogue::SWIGLU) {
+                swa[e] = sw_lds[64 * wn + 8 * epi_cg + e];
+                swb[e] = sw_lds[128 + 64 * wn + 8 * epi_cg + e];
+            } else {
+                swa[e] = sw_lds[128 * wn + 8 * epi_cg + e];
+                swb[e] = 0.0f;
+            }
+        }
+    }
 
     auto stash_block = [&](int a) {
         asm volatile("" ::: "memory");
@@ -374,13 +432,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         // lane -> 8 output columns (gate j, up i + j) and a row phase of 8
         uint16_t* y = reinterpret_cast<uint16_t*>(out);
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
+        for (int a = 0; a < MA; ++a) {
             stash_block(a);
 #pragma nounroll
             for (int it = 0; it < 4; ++it) {
                 const int lr = 8 * it + ro;
                 const int grow = grow0 + 32 * a + lr;
-                const float sxr = sx_lds[64 * wm + 32 * a + lr];
+                const float sxr = sx_lds[32 * MA * wm + 32 * a + lr];
                 const v4i g0 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg);
                 const v4i g1 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg + 4);
                 const v4i u0 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 64 + 8 * cg);
@@ -412,7 +470,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     } else {
         // lane -> 8 output columns and a row phase of 4
 #pragma unroll
-        for (int a = 0; a < 2; ++a) {
+        for (int a = 0; a < MA; ++a) {
             stash_block(a);
 #pragma nounroll
             for (int it = 0; it < 8; ++it) {
@@ -434,7 +492,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                     }
                 } else {
                     uint16_t* y = reinterpret_cast<uint16_t*>(out);
-                    const float sxr = sx_lds[64 * wm + 32 * a + lr];
+                    const float sxr = sx_lds[32 * MA * wm + 32 * a + lr];
                     const int av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
                     float h[8];
 #pragma unroll
