@@ -74,16 +74,16 @@ constexpr int PITCH = 136;
 constexpr int STASH_WAVE_BYTES = 32 * PITCH * 4;
 constexpr int STASH_BYTES = NWAVES * STASH_WAVE_BYTES;
 // as many ring stages (at most 4) as fit in 160 KiB of LDS with the stash
-// (which reuses the ring) and the tile's scales
+// (which reuses the ring) and the tile's row scales
 constexpr int lds_for(int stages) {
-    return (stages * STAGE_BYTES > STASH_BYTES ? stages * STAGE_BYTES : STASH_BYTES) + 4 * (BM + BN);
+    return (stages * STAGE_BYTES > STASH_BYTES ? stages * STAGE_BYTES : STASH_BYTES) + 4 * BM;
 }
 constexpr int STAGES = lds_for(4) <= 160 * 1024 ? 4 : 3;
 constexpr int RING_BYTES = STAGES * STAGE_BYTES;
 constexpr int LDS_BYTES = RING_BYTES > STASH_BYTES ? RING_BYTES : STASH_BYTES;
 constexpr int GROUP_M = 8;
 static_assert(BM % 128 == 0 && MA >= 2 && MA <= 3, "tile rows");
-static_assert(LDS_BYTES + 4 * (BM + BN) <= 160 * 1024, "LDS budget");
+static_assert(LDS_BYTES + 4 * BM <= 160 * 1024, "LDS budget");
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -158,7 +158,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     const float* __restrict__ sw, int M, int N, int K, void* __restrict__ out, int MT, int NT) {
     __shared__ __attribute__((aligned(1024))) int8_t lds[LDS_BYTES];
     __shared__ float sx_lds[BM];
-    __shared__ float sw_lds[BN];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -169,26 +168,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     const int m0 = tile.tm * BM;
     const int rows_a = (M - m0) < BM ? (M - m0) : BM;
 
-    // Epilogue scales go to LDS before the main loop (their loads complete
-    // under it): s_x of the tile's rows, and s_w of its 256 weight rows (for
-    // SwiGLU the 128 gate rows, then the matching 128 up rows).
+    // Epilogue scales, loaded before the main loop so that their latency is
+    // hidden: s_x of the tile's rows into LDS (read back per output row), and
+    // s_w of the lane's 8 output columns (gate and up columns for SwiGLU) into
+    // registers.  (Keeping these register loads outstanding across the main
+    // loop also keeps the compiler from draining the ring's copies before the
+    // first fragment read of every stage, as it does when no other vector
+    // load is pending there.)
     constexpr int EPI_CG = EP == Epilogue::SWIGLU ? 8 : 16;   // column groups per wave row
     const int epi_cg = lane % EPI_CG;
     const int epi_ro = lane / EPI_CG;
     const int epi_col0 = EP == Epilogue::SWIGLU ? tile.tn * (BN / 2) + 64 * wn + 8 * epi_cg
                                                 : tile.tn * BN + 128 * wn + 8 * epi_cg;
+    float swa[8], swb[8];
     if constexpr (EP != Epilogue::S32) {
-        for (int r = tid; r < BM; r += NTHREADS) sx_lds[r] = sx[r < rows_a ? m0 + r : M - 1];
-        if (tid < BN) {
-            int c;
-            if constexpr (EP == Epilogue::SWIGLU) {
-                const int j = tile.tn * (BN / 2) + (tid & 127);
-                c = (j < N ? j : N - 1) + (tid < 128 ? 0 : N);
-            } else {
-                const int j = tile.tn * BN + tid;
-                c = j < N ? j : N - 1;
-            }
-            sw_lds[tid] = sw[c];
+        if (tid < BM) sx_lds[tid] = sx[tid < rows_a ? m0 + tid : M - 1];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = (epi_col0 + e) < N ? (epi_col0 + e) : (N - 1);
+            swa[e] = sw[c];
+            swb[e] = EP == Epilogue::SWIGLU ? sw[N + c] : 0.0f;
         }
     }
 
@@ -297,13 +296,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     // At stage kt's barrier the stages after kt + 1 may stay in flight
     // (STAGES - 2 of them, COPIES copies each).  The steady-state loop runs
     // while a refill remains; the last stages are peeled so that the loop
-    // body is straight-line code.  K % 256 == 0, so KT >= 4 >= STAGES.
+    // body is straight-line code.
     constexpr int NREAD = MA + 4;        // fragment reads per k-step
     constexpr int NMFMA = 4 * MA;        // MFMAs per k-step
     const int KT = K / BK;
+    // (The conditional issue and the branch on the stages ahead are kept in
+    // this form on purpose: with an unconditional prologue the compiler
+    // inserts a full vmcnt(0) before the first fragment read of every stage
+    // of the main loop, which drains the prefetch.)
 #pragma unroll
-    for (int st = 0; st < STAGES; ++st) issue(st, st);
-    wait_vmcnt<(STAGES - 1) * COPIES>();
+    for (int st = 0; st < STAGES; ++st)
+        if (st < KT) issue(st, st);
+    {
+        const int ahead = (KT - 1) < (STAGES - 1) ? (KT - 1) : (STAGES - 1);
+        if (STAGES >= 4 && ahead >= 3) wait_vmcnt<(STAGES >= 4 ? 3 : 2) * COPIES>();
+        else if (ahead >= 2) wait_vmcnt<2 * COPIES>();
+        else if (ahead == 1) wait_vmcnt<COPIES>();
+        else wait_vmcnt<0>();
+    }
     lds_barrier();
 
     int kt = 0;
@@ -399,19 +409,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     lds_barrier();   // every wave is done reading the ring
     int32_t* stash = reinterpret_cast<int32_t*>(lds + wave * STASH_WAVE_BYTES);
     const int grow0 = m0 + 32 * MA * wm;
-    float swa[8], swb[8];   // the lane's column scales (gate and up for SwiGLU)
-    if constexpr (EP != Epilogue::S32) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            if constexpr (EP == Epilogue::SWIGLU) {
-                swa[e] = sw_lds[64 * wn + 8 * epi_cg + e];
-                swb[e] = sw_lds[128 + 64 * wn + 8 * epi_cg + e];
-            } else {
-                swa[e] = sw_lds[128 * wn + 8 * epi_cg + e];
-                swb[e] = 0.0f;
-            }
-        }
-    }
+
 
     auto stash_block = [&](int a) {
         asm volatile("" ::: "memory");
