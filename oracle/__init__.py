@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         L.orc_swiglu_rotate_quant_rows.restype = ctypes.c_int
         L.orc_dequantize_weight.argtypes = [P, P, I64, I64, P]
         L.orc_lora_add.argtypes = [P, I64, I64, P, P, I64, ctypes.c_float]
+        L.orc_attention_rows.argtypes = [P, P, I64, P, P, P, I64, I64, P, P]
         _lib = L
     return _lib
 
@@ -308,3 +309,58 @@ def linear_swiglu_rows(x_bf16, q_w, s_w, rows=None):
     qx, sx = rotate_quant_act(x_bf16, rows)
     acc = gemm_s32(qx, q_w)
     return swiglu_bf16(acc, sx, s_w)
+
+
+# ------------------------------------------------------------------ attention
+
+def attention_quant(x_bf16: np.ndarray):
+    """Per token-head int8 quantization of Q or K: raw bf16 [rows, d] -> codes
+    [rows, d], scales [rows] (the per-row quantizer, no rotation)."""
+    return quantize_rows(bf16_to_f32(x_bf16))
+
+
+def to_fp16(x_bf16: np.ndarray) -> np.ndarray:
+    """bf16 bits -> fp16 values, round to nearest even (numpy's cast)."""
+    return bf16_to_f32(x_bf16).astype(np.float16)
+
+
+def attention_rows(qc, sq, kc, sk, v_f16):
+    """One head: O [nq, d] and the rounding scale sum p|v|/sum p, both fp64,
+    for query codes qc [nq, d] / scales sq against all keys kc [s, d] / sk and
+    fp16 values v_f16 [s, d]."""
+    qc = np.ascontiguousarray(qc, dtype=np.int8)
+    kc = np.ascontiguousarray(kc, dtype=np.int8)
+    sq = np.ascontiguousarray(sq, dtype=np.float32)
+    sk = np.ascontiguousarray(sk, dtype=np.float32)
+    v = np.ascontiguousarray(np.asarray(v_f16, dtype=np.float16), dtype=np.float64)
+    nq, d = qc.shape
+    s = kc.shape[0]
+    assert kc.shape == (s, d) and v.shape == (s, d) and sq.size == nq and sk.size == s
+    out = np.empty((nq, d), np.float64)
+    absw = np.empty((nq, d), np.float64)
+    lib().orc_attention_rows(_p(qc), _p(sq), nq, _p(kc), _p(sk), _p(v), s, d, _p(out), _p(absw))
+    return out, absw
+
+
+def split_heads(x_bf16: np.ndarray, heads: int) -> np.ndarray:
+    """[s, heads * d] -> [heads, s, d] (a view change, no arithmetic)."""
+    s, w = x_bf16.shape
+    return np.ascontiguousarray(x_bf16.reshape(s, heads, w // heads).transpose(1, 0, 2))
+
+
+def attention(q_bf16, k_bf16, v_bf16, heads: int, rows=None):
+    """Full attention of [s, heads * d] bf16 Q, K, V (raw bits): per head,
+    quantize Q and K, convert V to fp16, softmax-attend.  Returns O [heads,
+    nq, d] fp64, absw likewise, and the codes/scales (qc, sq, kc, sk) per head.
+    ``rows`` restricts the queries (all keys are always used)."""
+    qh, kh, vh = (split_heads(t, heads) for t in (q_bf16, k_bf16, v_bf16))
+    outs, absws, qcs, sqs, kcs, sks = [], [], [], [], [], []
+    for h in range(heads):
+        qc, sq = attention_quant(qh[h])
+        kc, sk = attention_quant(kh[h])
+        sel = slice(None) if rows is None else np.asarray(rows, np.int64)
+        o, a = attention_rows(qc[sel], sq[sel], kc, sk, to_fp16(vh[h]))
+        outs.append(o); absws.append(a)
+        qcs.append(qc); sqs.append(sq); kcs.append(kc); sks.append(sk)
+    return (np.stack(outs), np.stack(absws),
+            (np.stack(qcs), np.stack(sqs), np.stack(kcs), np.stack(sks)))

@@ -25,6 +25,8 @@
  *     (one scale per token), the Hadamard rotation runs inside that quantizer,
  *     the GEMM writes bf16 directly, and fc1's gate/up rows are paired so that
  *     SwiGLU is applied in the GEMM epilogue.
+ *   - h3-rs README, "Speed": the DiT's attention multiplies int8 Q by int8 K^T
+ *     and fp16 P by fp16 V (see orc_attention_rows for the readings).
  * Every step the pages leave open is a stated reading (see the comment at each
  * function): Sylvester ordering, orthonormal scaling 1/16, contiguous groups,
  * symmetric absmax/127 scales, round-half-even, (acc*s_x)*s_w dequant order,
@@ -401,5 +403,60 @@ void orc_lora_add(float* w, int64_t n, int64_t k, const float* b, const float* a
             for (int64_t j = 0; j < rank; ++j) acc = fmaf(b[r * rank + j], a[j * k + c], acc);
             w[r * k + c] = w[r * k + c] + scale * acc;
         }
+    }
+}
+
+/* ---------------------------------------------------- int8 Q.K^T / fp16 P.V
+ *
+ * The DiT's attention as h3-rs runs it (h3-rs README, "Speed": the logits come
+ * from an int8 Q.K^T, the value product is an fp16 P.V), over the full
+ * sequence with no mask (hybrid model card, "Notes and limitations": the
+ * evaluated implementation uses full attention).
+ *
+ * Readings (the pages give only the operand types):
+ *   - Q and K are quantized per token and per head: each head's d values of a
+ *     token form one row for the per-row quantizer above, without rotation
+ *     (the pages name no rotation for attention).
+ *   - logit_ij = acc_ij * s_q[i] * s_k[j] / sqrt(d), acc_ij the exact integer
+ *     dot product of the codes; softmax over all keys j.
+ *   - V enters as fp16 values (the caller converts), the output is
+ *     O_i = sum_j p_ij v_j / sum_j p_ij with p_ij = exp(logit_ij - max_j).
+ * Everything after the integer dot product is evaluated in fp64, so this is
+ * the definition itself; the kernel's fp32 logits, fp16 probabilities and
+ * fp32 sums differ from it by rounding only.  absw receives
+ * sum_j p_ij |v_jc| / sum_j p_ij, the scale of that rounding per output. */
+void orc_attention_rows(const int8_t* qc, const float* sq, int64_t nq, const int8_t* kc,
+                        const float* sk, const double* v, int64_t s, int64_t d, double* out,
+                        double* absw) {
+    const double inv_sqrt_d = 1.0 / sqrt((double)d);
+    int64_t i;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (i = 0; i < nq; ++i) {
+        double* logit = (double*)malloc((size_t)(s > 0 ? s : 1) * sizeof(double));
+        double mx = -INFINITY;
+        for (int64_t j = 0; j < s; ++j) {
+            int32_t acc = 0;
+            for (int64_t c = 0; c < d; ++c) acc += (int32_t)qc[i * d + c] * (int32_t)kc[j * d + c];
+            logit[j] = (double)acc * (double)sq[i] * (double)sk[j] * inv_sqrt_d;
+            if (logit[j] > mx) mx = logit[j];
+        }
+        double z = 0.0;
+        for (int64_t c = 0; c < d; ++c) {
+            out[i * d + c] = 0.0;
+            absw[i * d + c] = 0.0;
+        }
+        for (int64_t j = 0; j < s; ++j) {
+            const double p = exp(logit[j] - mx);
+            z += p;
+            for (int64_t c = 0; c < d; ++c) {
+                out[i * d + c] += p * v[j * d + c];
+                absw[i * d + c] += p * fabs(v[j * d + c]);
+            }
+        }
+        for (int64_t c = 0; c < d; ++c) {
+            out[i * d + c] /= z;
+            absw[i * d + c] /= z;
+        }
+        free(logit);
     }
 }

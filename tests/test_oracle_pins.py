@@ -696,3 +696,132 @@ def test_lora_add_rounding_bound():
     bound = (abs(float(scale)) * (gamma * (np.abs(b).astype(np.float64) @ np.abs(a).astype(np.float64))
                                   + 2 * U * np.abs(d64)) + 2 * U * np.abs(ref))
     assert np.all(np.abs(got - ref) <= bound)
+
+
+# ------------------------------------------------------------------ attention
+
+def _attn(qc, sq, kc, sk, v):
+    return oracle.attention_rows(np.asarray(qc, np.int8), np.asarray(sq, np.float32),
+                                 np.asarray(kc, np.int8), np.asarray(sk, np.float32),
+                                 np.asarray(v, np.float16))
+
+
+def test_attention_two_keys_closed_form():
+    """Hand-derived: d = 4 (so 1/sqrt(d) = 1/2), q = (1, 2, 3, 4) with s_q =
+    1/8; k_0 = (4, 3, 2, 1) with s_k = 1/4, k_1 = (-1, 0, 1, 0) with s_k = 1/2.
+    Integer dots 20 and 2, logits 20/64 = 0.3125 and 2/32 = 0.0625, so the
+    first key's weight is the logistic of 0.25.  A wrong sign, a dropped
+    1/sqrt(d), a scale taken from the wrong index or a transposed code matrix
+    each changes the weight."""
+    v = np.array([[1.0, -2.0, 0.5, 8.0], [3.0, 4.0, -0.25, 0.0]])
+    o, a = _attn([[1, 2, 3, 4]], [0.125], [[4, 3, 2, 1], [-1, 0, 1, 0]], [0.25, 0.5], v)
+    w0 = 1.0 / (1.0 + math.exp(-0.25))
+    ref = w0 * v[0] + (1.0 - w0) * v[1]
+    assert np.allclose(o[0], ref, rtol=1e-15, atol=1e-15)
+    assert np.allclose(a[0], w0 * np.abs(v[0]) + (1 - w0) * np.abs(v[1]), rtol=1e-15, atol=1e-15)
+
+
+def test_attention_uniform_keys_and_zero_query():
+    """Identical keys (codes and scale), or an all-zero query (s_q = 0): every
+    logit is equal, so the output is the plain mean of the values."""
+    rng = np.random.default_rng(60)
+    s, d = 37, 128
+    v = rng.integers(-64, 65, size=(s, d)) / 8.0
+    kc_row = rng.integers(-127, 128, size=d)
+    kc = np.tile(kc_row, (s, 1))
+    qc = rng.integers(-127, 128, size=(3, d))
+    o, _ = _attn(qc, [0.01, 0.5, 3.0], kc, np.full(s, 0.02), v)
+    assert np.allclose(o, np.tile(v.mean(axis=0), (3, 1)), rtol=1e-14, atol=1e-14)
+    kc2 = rng.integers(-127, 128, size=(s, d))
+    o2, _ = _attn(qc[:1], [0.0], kc2, rng.uniform(0.01, 0.1, s), v)
+    assert np.allclose(o2[0], v.mean(axis=0), rtol=1e-14, atol=1e-14)
+
+
+def test_attention_large_logits_keep_finite():
+    """Logits near 894 (exp would overflow without the max subtraction); two
+    keys share the codes and differ in scale, so the weight of the first is
+    the logistic of the logit difference, computed here from the definition's
+    logits in fp64."""
+    d = 128
+    q = np.full((1, d), 127)
+    kc = np.full((2, d), 127)
+    sq, sk = np.float32(0.07), np.array([0.07, 0.0699], np.float32)
+    acc = 127 * 127 * d
+    l = [acc * float(sq) * float(x) / math.sqrt(d) for x in sk]
+    assert l[0] > 800
+    v = np.array([np.full(d, 1.0), np.full(d, -1.0)])
+    o, _ = _attn(q, [sq], kc, sk, v)
+    w0 = 1.0 / (1.0 + math.exp(-(l[0] - l[1])))
+    assert np.all(np.isfinite(o))
+    assert np.allclose(o[0], w0 - (1 - w0), rtol=1e-12, atol=1e-12)
+
+
+def test_attention_key_permutation_and_affine_values():
+    """Keys are a set: permuting key codes, key scales and value rows together
+    leaves the output unchanged; the weights sum to one, so values 2 v + 1
+    (exact in fp16 here) give 2 O + 1, and each output lies between the
+    smallest and largest value of its column."""
+    rng = np.random.default_rng(61)
+    nq, s, d = 5, 41, 128
+    qc = rng.integers(-127, 128, size=(nq, d))
+    kc = rng.integers(-127, 128, size=(s, d))
+    sq = rng.uniform(0.001, 0.01, nq)
+    sk = rng.uniform(0.001, 0.01, s)
+    v = rng.integers(-64, 65, size=(s, d)) / 8.0
+    o, _ = _attn(qc, sq, kc, sk, v)
+    p = rng.permutation(s)
+    o_p, _ = _attn(qc, sq, kc[p], sk[p], v[p])
+    assert np.allclose(o_p, o, rtol=1e-13, atol=1e-13)
+    o_a, _ = _attn(qc, sq, kc, sk, 2 * v + 1)
+    assert np.allclose(o_a, 2 * o + 1, rtol=1e-13, atol=1e-13)
+    assert np.all(o >= v.min(axis=0) - 1e-12) and np.all(o <= v.max(axis=0) + 1e-12)
+    # the logits are not flat here (else the checks above say little)
+    assert np.abs(o - v.mean(axis=0)).max() > 0.1
+
+
+def test_attention_bruteforce_decimal():
+    """Tiny random case against 40-digit decimal arithmetic from the integer
+    codes and the exact binary values of the fp32 scales."""
+    import decimal
+    from fractions import Fraction
+    decimal.getcontext().prec = 40
+    D = decimal.Decimal
+    rng = np.random.default_rng(62)
+    nq, s, d = 3, 6, 8
+    qc = rng.integers(-127, 128, size=(nq, d))
+    kc = rng.integers(-127, 128, size=(s, d))
+    sq = rng.uniform(0.005, 0.03, nq).astype(np.float32)
+    sk = rng.uniform(0.005, 0.03, s).astype(np.float32)
+    v = (rng.standard_normal((s, d))).astype(np.float16)
+    o, _ = _attn(qc, sq, kc, sk, v)
+    root_d = D(d).sqrt()
+    for i in range(nq):
+        logits = []
+        for j in range(s):
+            acc = int(np.dot(qc[i].astype(np.int64), kc[j].astype(np.int64)))
+            f = Fraction(acc) * Fraction(float(sq[i])) * Fraction(float(sk[j]))
+            logits.append(D(f.numerator) / D(f.denominator) / root_d)
+        m = max(logits)
+        p = [(x - m).exp() for x in logits]
+        z = sum(p)
+        for c in range(d):
+            ref = sum(p[j] * D(float(v[j, c])) for j in range(s)) / z
+            assert abs(o[i, c] - float(ref)) <= 1e-13 * (1 + abs(float(ref))), (i, c)
+
+
+def test_attention_quant_is_the_per_row_quantizer():
+    """Q and K codes: the per-row absmax/127 quantizer on the widened bf16
+    values of each token's head slice, bit for bit against an exact-rational
+    evaluation of rint(v / s) with s = RN(max|v| / 127)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(63)
+    x = workloads.to_bf16_bits(rng.standard_normal((20, 128)).astype(np.float32) * 3)
+    q, s = oracle.attention_quant(x)
+    f = oracle.bf16_to_f32(x)
+    for r in range(20):
+        amax = np.abs(f[r]).max()
+        assert s[r] == np.float32(amax) / np.float32(127.0)
+        for c in range(128):
+            t = Fraction(float(f[r, c])) / Fraction(float(s[r]))
+            n = round(t)          # Python rounds exact halves to even
+            assert q[r, c] == max(-127, min(127, n)), (r, c)
