@@ -195,6 +195,64 @@ int convrot_merge_lora(const int8_t* q_w, const float* s_w, int64_t n, int64_t k
                        int8_t* q_out, float* s_out, void* workspace, size_t workspace_bytes,
                        void* stream);
 
+/* ------------------------------------------------------------------------
+ * int8 Q.K^T / fp16 P.V attention (h3-rs README, "Speed": the DiT's attention
+ * is one flash kernel with an int8 Q.K^T and an fp16 P.V; Minimax_h3_hybrid
+ * model card, "Notes and limitations": full attention, no mask).
+ *
+ * Q, K, V are [s, ld] bf16 row-major with head h at columns
+ * [h * 128, h * 128 + 128) -- the thirds of the fused QKV projection's output
+ * may be passed directly (ld = 3 * heads * 128).  Head dimension 128 only.
+ *   quantize   per token and head, as the layer's per-row quantizer without
+ *              rotation: s = max|x| / 127 over the head's 128 values
+ *              (correctly rounded fp32), codes rint(x / s), half to even,
+ *              s == 0 gives zero codes;
+ *   logits     acc_ij * s_q[i] * s_k[j] / sqrt(128), acc_ij the exact int32
+ *              dot product of the codes (evaluated in fp32, base 2);
+ *   softmax    over all s keys, probabilities rounded to fp16;
+ *   output     O_i = sum_j p_ij v_j / sum_j p_ij with V rounded to fp16 (RNE),
+ *              fp32 sums, written as bf16 (RNE) to out [s, ld_out], head h at
+ *              columns [h * 128, h * 128 + 128).
+ * The codes and scales are bit-exact; the output agrees with the fp64
+ * evaluation of the same definition to the rounding of the fp16 probabilities,
+ * the fp32 sums and the bf16 store.
+ *
+ * Shapes: 0 <= s <= 2^24, heads >= 0, head_dim == 128; ld and ld_out are
+ * multiples of 8 and at least heads * 128.  s == 0 or heads == 0 is success
+ * with nothing enqueued.  V values beyond the fp16 range give unspecified
+ * outputs.  The output must not overlap the inputs or the workspace.
+ * ------------------------------------------------------------------------ */
+#define CONVROT_ATTN_HEAD_DIM 128
+
+/* Workspace of the attention of s tokens and `heads` heads; returns its size
+ * in bytes (0 for invalid sizes).  If `offsets` is not NULL it receives the
+ * byte offsets of the five regions (each 256-byte aligned), s_pad being s
+ * rounded up to a multiple of 64:
+ *   [0] Q codes   int8 [heads][s][128]
+ *   [1] Q scales  fp32 [heads][s]
+ *   [2] K codes   int8 [heads][s_pad][128]   (rows past s are zero)
+ *   [3] K scales  fp32 [heads][s_pad]        (zero past s)
+ *   [4] V         fp16 [heads][s_pad / 64][128][64]: per block of 64 keys,
+ *                 row d holds head dimension d of the 64 keys, key j of each
+ *                 32 at position j with bits 2 and 3 swapped (zero past s). */
+size_t convrot_attention_workspace(int64_t s, int64_t heads, int64_t head_dim, size_t offsets[5]);
+
+/* Step 1: quantize Q and K and lay out V in the workspace.                  */
+int convrot_attention_prep(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld,
+                           int64_t s, int64_t heads, int64_t head_dim, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* Step 2: attention over a workspace filled by convrot_attention_prep with
+ * the same s and heads.                                                      */
+int convrot_attention_prepared(const void* workspace, size_t workspace_bytes, int64_t s,
+                               int64_t heads, int64_t head_dim, uint16_t* out, int64_t ld_out,
+                               void* stream);
+
+/* Both steps in order on the stream.                                        */
+int convrot_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld, int64_t s,
+                      int64_t heads, int64_t head_dim, uint16_t* out, int64_t ld_out,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL).         */
 const char* convrot_status_string(int status);
 

@@ -8,9 +8,14 @@ gfx950 behind the C ABI of include/convrot.h; this package is its Python
 binding (torch provides device memory and the stream).
 """
 from ._lib import (  # noqa: F401
+    ATTN_HEAD_DIM,
     GROUP,
     MAX_K,
     ConvRotError,
+    attention,
+    attention_prep,
+    attention_prepared,
+    attention_workspace,
     dequantize_weight,
     gemm_dequant,
     gemm_s32,

@@ -27,7 +27,11 @@ SYMBOLS = (
     "convrot_linear", "convrot_linear_swiglu", "convrot_gemm_dequant", "convrot_gemm_swiglu",
     "convrot_gemm_s32", "convrot_swiglu_rotate_quant_act", "convrot_dequantize_weight",
     "convrot_lora_add", "convrot_merge_workspace_bytes", "convrot_merge_lora", "convrot_status_string",
+    "convrot_attention_workspace", "convrot_attention_prep", "convrot_attention_prepared",
+    "convrot_attention",
 )
+
+ATTN_HEAD_DIM = 128
 
 
 class ConvRotError(RuntimeError):
@@ -66,6 +70,10 @@ def load_library() -> ctypes.CDLL:
             "convrot_merge_workspace_bytes": ([I64, I64], SZ),
             "convrot_merge_lora": ([P, P, I64, I64, P, P, I64, ctypes.c_float, P, P, P, SZ, P], I),
             "convrot_status_string": ([I], ctypes.c_char_p),
+            "convrot_attention_workspace": ([I64, I64, I64, P], SZ),
+            "convrot_attention_prep": ([P, P, P, I64, I64, I64, I64, P, SZ, P], I),
+            "convrot_attention_prepared": ([P, SZ, I64, I64, I64, P, I64, P], I),
+            "convrot_attention": ([P, P, P, I64, I64, I64, I64, P, I64, P, SZ, P], I),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -297,3 +305,87 @@ def merge_lora(q_w: torch.Tensor, s_w: torch.Tensor, lora_b: torch.Tensor, lora_
         q_w.data_ptr(), s_w.data_ptr(), n, k, lora_b.data_ptr(), lora_a.data_ptr(), rank, float(scale),
         q_out.data_ptr(), s_out.data_ptr(), workspace.data_ptr(), workspace.numel(), _stream()))
     return q_out, s_out
+
+
+# ------------------------------------------------------------------ attention
+
+def attention_workspace(s: int, heads: int):
+    """(bytes, offsets of the five regions) of the attention workspace for s
+    tokens and ``heads`` heads of dimension 128 (see convrot.h)."""
+    off = (ctypes.c_size_t * 5)()
+    n = int(load_library().convrot_attention_workspace(int(s), int(heads), ATTN_HEAD_DIM, off))
+    if n == 0 and (s != 0 and heads != 0):
+        raise ValueError("invalid attention sizes s=%d heads=%d" % (s, heads))
+    return n, [int(x) for x in off]
+
+
+def _rows_view(t: torch.Tensor, name: str) -> int:
+    """Row stride of a 2-D bf16 GPU tensor whose rows are contiguous (a column
+    slice of a wider matrix is allowed)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if t.dtype != torch.bfloat16:
+        raise TypeError("%s must be bfloat16 (got %s)" % (name, t.dtype))
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError("%s must be 2-D with unit column stride" % name)
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def _attn_inputs(q, k, v, heads):
+    ld = _rows_view(q, "q")
+    for t, nm in ((k, "k"), (v, "v")):
+        if _rows_view(t, nm) != ld and t.shape[0] > 1:
+            raise ValueError("q, k and v must share one row stride")
+        if tuple(t.shape) != tuple(q.shape):
+            raise ValueError("q, k and v must have one shape (got %s, %s)" % (tuple(q.shape), tuple(t.shape)))
+    s, w = q.shape
+    if w != heads * ATTN_HEAD_DIM:
+        raise ValueError("q has %d columns, expected heads * 128 = %d" % (w, heads * ATTN_HEAD_DIM))
+    return s, ld
+
+
+def _attn_workspace(workspace, s, heads, like):
+    need, _ = attention_workspace(s, heads)
+    if workspace is None:
+        return torch.empty(max(need, 16), dtype=torch.uint8, device=like.device)
+    if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.dtype == torch.uint8
+            and workspace.is_contiguous()):
+        raise TypeError("workspace must be a contiguous uint8 GPU tensor")
+    return workspace
+
+
+def attention_prep(q, k, v, heads: int, workspace=None):
+    """Quantize Q and K per token-head and lay out V (fp16) in the workspace
+    (a uint8 GPU tensor, allocated if None); returns the workspace."""
+    s, ld = _attn_inputs(q, k, v, heads)
+    ws = _attn_workspace(workspace, s, heads, q)
+    _check("convrot_attention_prep", load_library().convrot_attention_prep(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), ld, s, heads, ATTN_HEAD_DIM, ws.data_ptr(),
+        ws.numel(), _stream()))
+    return ws
+
+
+def attention_prepared(workspace, s: int, heads: int, out=None):
+    """Attention over a prepared workspace -> bf16 [s, heads * 128]."""
+    if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.dtype == torch.uint8
+            and workspace.is_contiguous()):
+        raise TypeError("workspace must be a contiguous uint8 GPU tensor")
+    o = _out(out, (s, heads * ATTN_HEAD_DIM), torch.bfloat16, workspace, "out")
+    _check("convrot_attention_prepared", load_library().convrot_attention_prepared(
+        workspace.data_ptr(), workspace.numel(), s, heads, ATTN_HEAD_DIM, o.data_ptr(),
+        heads * ATTN_HEAD_DIM, _stream()))
+    return o
+
+
+def attention(q, k, v, heads: int, out=None, workspace=None):
+    """int8 Q.K^T / fp16 P.V attention of bf16 [s, heads * 128] Q, K, V (column
+    slices of one QKV matrix are accepted) -> bf16 [s, heads * 128]."""
+    s, ld = _attn_inputs(q, k, v, heads)
+    ws = _attn_workspace(workspace, s, heads, q)
+    o = _out(out, (s, heads * ATTN_HEAD_DIM), torch.bfloat16, q, "out")
+    _check("convrot_attention", load_library().convrot_attention(
+        q.data_ptr(), k.data_ptr(), v.data_ptr(), ld, s, heads, ATTN_HEAD_DIM, o.data_ptr(),
+        heads * ATTN_HEAD_DIM, ws.data_ptr(), ws.numel(), _stream()))
+    return o

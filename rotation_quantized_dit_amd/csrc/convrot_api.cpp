@@ -227,3 +227,98 @@ int convrot_linear_swiglu(const uint16_t* x, int64_t m, int64_t k, const int8_t*
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ attention
+
+namespace {
+
+constexpr int64_t kAttnMaxS = (int64_t)1 << 24;
+
+inline size_t align256(size_t x) { return (x + 255u) & ~(size_t)255u; }
+
+// Region offsets of the attention workspace (see convrot.h); returns the
+// total size, or 0 for invalid sizes.
+bool attn_sizes_ok(int64_t s, int64_t heads, int64_t head_dim) {
+    return s >= 0 && s <= kAttnMaxS && heads >= 0 && head_dim == CONVROT_ATTN_HEAD_DIM &&
+           heads <= (int64_t)INT32_MAX / (kAttnMaxS / 64);
+}
+
+size_t attn_layout(int64_t s, int64_t heads, int64_t head_dim, size_t off[5]) {
+    if (!attn_sizes_ok(s, heads, head_dim)) return 0;
+    const size_t S = (size_t)s, H = (size_t)heads, P = (size_t)convrot::attn_pad_keys(s);
+    size_t o[6];
+    o[0] = 0;
+    o[1] = align256(o[0] + H * S * 128);
+    o[2] = align256(o[1] + H * S * 4);
+    o[3] = align256(o[2] + H * P * 128);
+    o[4] = align256(o[3] + H * P * 4);
+    o[5] = align256(o[4] + H * P * 128 * 2);
+    if (off)
+        for (int i = 0; i < 5; ++i) off[i] = o[i];
+    return o[5];
+}
+
+int check_attn(int64_t s, int64_t heads, int64_t head_dim, int64_t ld) {
+    if (!attn_sizes_ok(s, heads, head_dim)) return CONVROT_ERR_SHAPE;
+    if (ld < heads * CONVROT_ATTN_HEAD_DIM || (ld % 8) != 0) return CONVROT_ERR_SHAPE;
+    return CONVROT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t convrot_attention_workspace(int64_t s, int64_t heads, int64_t head_dim, size_t offsets[5]) {
+    return attn_layout(s, heads, head_dim, offsets);
+}
+
+int convrot_attention_prep(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld,
+                           int64_t s, int64_t heads, int64_t head_dim, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (int st = check_attn(s, heads, head_dim, ld)) return st;
+    if (s == 0 || heads == 0) return CONVROT_OK;
+    if (!q || !k || !v) return CONVROT_ERR_NULL;
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v)) return CONVROT_ERR_ALIGN;
+    size_t off[5];
+    const size_t need = attn_layout(s, heads, head_dim, off);
+    if (!workspace || workspace_bytes < need) return CONVROT_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return CONVROT_ERR_ALIGN;
+    uint8_t* w = (uint8_t*)workspace;
+    return launched(convrot::launch_attn_prep(q, k, v, ld, s, heads, (int8_t*)(w + off[0]),
+                                              (float*)(w + off[1]), (int8_t*)(w + off[2]),
+                                              (float*)(w + off[3]), w + off[4], (hipStream_t)stream));
+}
+
+int convrot_attention_prepared(const void* workspace, size_t workspace_bytes, int64_t s,
+                               int64_t heads, int64_t head_dim, uint16_t* out, int64_t ld_out,
+                               void* stream) {
+    if (int st = check_attn(s, heads, head_dim, ld_out)) return st;
+    if (s == 0 || heads == 0) return CONVROT_OK;
+    if (!out) return CONVROT_ERR_NULL;
+    if (!aligned16(out)) return CONVROT_ERR_ALIGN;
+    size_t off[5];
+    const size_t need = attn_layout(s, heads, head_dim, off);
+    if (!workspace || workspace_bytes < need) return CONVROT_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return CONVROT_ERR_ALIGN;
+    const uint8_t* w = (const uint8_t*)workspace;
+    return launched(convrot::launch_attn_flash((const int8_t*)(w + off[0]), (const float*)(w + off[1]),
+                                               (const int8_t*)(w + off[2]), (const float*)(w + off[3]),
+                                               w + off[4], s, heads, out, ld_out, (hipStream_t)stream));
+}
+
+int convrot_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld, int64_t s,
+                      int64_t heads, int64_t head_dim, uint16_t* out, int64_t ld_out,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (int st = check_attn(s, heads, head_dim, ld)) return st;
+    if (int st = check_attn(s, heads, head_dim, ld_out)) return st;
+    if (s == 0 || heads == 0) return CONVROT_OK;
+    if (!out) return CONVROT_ERR_NULL;
+    if (!aligned16(out)) return CONVROT_ERR_ALIGN;
+    if (int st = convrot_attention_prep(q, k, v, ld, s, heads, head_dim, workspace, workspace_bytes,
+                                        stream))
+        return st;
+    return convrot_attention_prepared(workspace, workspace_bytes, s, heads, head_dim, out, ld_out,
+                                      stream);
+}
+
+}  // extern "C"

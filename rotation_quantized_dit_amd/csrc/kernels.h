@@ -32,4 +32,17 @@ hipError_t launch_gemm(Epilogue ep, const int8_t* q_x, const float* s_x, const i
                        const float* s_w, int64_t m, int64_t n, int64_t k, void* out,
                        hipStream_t stream);
 
+// K-ATTN: int8 Q.K^T / fp16 P.V attention, head dimension 128.  Keys are
+// padded to attn_pad_keys(s) (a multiple of 64).  prep: q/k/v are [s, ld]
+// bf16 with head h at columns [128 h, 128 h + 128); writes qc [heads][s][128],
+// sq [heads][s], kc [heads][s_pad][128], sk [heads][s_pad] and V^T blocks
+// vt [heads][s_pad / 64][128][64] (fp16).  flash: out [s, ld_out] bf16.
+int64_t attn_pad_keys(int64_t s);
+hipError_t launch_attn_prep(const uint16_t* q, const uint16_t* k, const uint16_t* v, int64_t ld,
+                            int64_t s, int64_t heads, int8_t* qc, float* sq, int8_t* kc, float* sk,
+                            void* vt, hipStream_t stream);
+hipError_t launch_attn_flash(const int8_t* qc, const float* sq, const int8_t* kc, const float* sk,
+                             const void* vt, int64_t s, int64_t heads, uint16_t* out, int64_t ld_out,
+                             hipStream_t stream);
+
 }  // namespace convrot

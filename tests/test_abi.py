@@ -185,3 +185,38 @@ def test_weight_ops_validation(L):
     assert L.convrot_merge_lora(A, None, 4, 256, C, D, 2, 1.0, A, B, D, need, None) == ERR_NULL
     assert L.convrot_merge_lora(A, B, 4, 257, C, D, 2, 1.0, A, B, D, need, None) == ERR_SHAPE
     assert L.convrot_merge_lora(None, None, 0, 256, None, None, 2, 1.0, None, None, None, 0, None) == OK
+
+
+def test_attention_validation(L):
+    """Attention entry points: sizes, head dimension, strides, pointers and the
+    workspace are checked on the host; empty calls are no-ops."""
+    from rotation_quantized_dit_amd._lib import ERR_ALIGN, ERR_NULL, ERR_SHAPE, ERR_WORKSPACE, OK
+    off = (ctypes.c_size_t * 5)()
+    need = L.convrot_attention_workspace(65, 2, 128, off)
+    s_pad = 128
+    assert list(off) == [0, 16640, 17408, 17408 + 2 * s_pad * 128, 50176 + 1024]
+    assert need == off[4] + 2 * s_pad * 128 * 2
+    assert L.convrot_attention_workspace(65, 2, 64, None) == 0
+    assert L.convrot_attention_workspace(-1, 2, 128, None) == 0
+    assert L.convrot_attention_workspace((1 << 24) + 1, 1, 128, None) == 0
+    assert L.convrot_attention_workspace(0, 5, 128, None) == 0
+    ld = 3 * 2 * 128
+    assert L.convrot_attention_prep(A, B, C, ld, 65, 2, 64, D, need, None) == ERR_SHAPE
+    assert L.convrot_attention_prep(A, B, C, 255, 65, 2, 128, D, need, None) == ERR_SHAPE
+    assert L.convrot_attention_prep(A, B, C, 128, 65, 2, 128, D, need, None) == ERR_SHAPE
+    assert L.convrot_attention_prep(A, B, C, ld, -3, 2, 128, D, need, None) == ERR_SHAPE
+    assert L.convrot_attention_prep(None, B, C, ld, 65, 2, 128, D, need, None) == ERR_NULL
+    assert L.convrot_attention_prep(MIS, B, C, ld, 65, 2, 128, D, need, None) == ERR_ALIGN
+    assert L.convrot_attention_prep(A, B, C, ld, 65, 2, 128, D, need - 1, None) == ERR_WORKSPACE
+    assert L.convrot_attention_prep(A, B, C, ld, 65, 2, 128, None, need, None) == ERR_WORKSPACE
+    assert L.convrot_attention_prep(A, B, C, ld, 65, 2, 128, MIS, need, None) == ERR_ALIGN
+    assert L.convrot_attention_prepared(D, need, 65, 2, 128, None, 256, None) == ERR_NULL
+    assert L.convrot_attention_prepared(D, need, 65, 2, 128, A, 200, None) == ERR_SHAPE
+    assert L.convrot_attention_prepared(D, need - 1, 65, 2, 128, A, 256, None) == ERR_WORKSPACE
+    assert L.convrot_attention_prepared(D, need, 65, 2, 128, MIS, 256, None) == ERR_ALIGN
+    assert L.convrot_attention(A, B, C, ld, 65, 2, 128, None, 256, D, need, None) == ERR_NULL
+    assert L.convrot_attention(A, B, C, ld, 65, 2, 128, A, 100, D, need, None) == ERR_SHAPE
+    # empty calls: nothing enqueued, NULL pointers allowed
+    assert L.convrot_attention(None, None, None, 768, 0, 2, 128, None, 256, None, 0, None) == OK
+    assert L.convrot_attention_prep(None, None, None, 0, 10, 0, 128, None, 0, None) == OK
+    assert L.convrot_attention_prepared(None, 0, 0, 3, 128, None, 384, None) == OK

@@ -56,6 +56,13 @@ WORKLOADS = {
 }
 
 
+# Attention: the DiT's 5376-wide hidden state split into 42 heads of 128 (the
+# pages give neither the head count nor the head dimension; 128 x 42 = 5376).
+ATTN_HEADS = 42
+ATTN_HEAD_DIM = 128
+ATTN_SEED = 5
+
+
 def to_bf16_bits(a: np.ndarray) -> np.ndarray:
     """fp32 array -> raw bf16 bits (uint16) via torch's round-to-nearest-even cast."""
     import torch
@@ -168,3 +175,31 @@ def sample_rows(m: int, seed: int, count: int = 64) -> np.ndarray:
         rows.update(range(VIDEO_TOKENS, m, 16))
     rows.update(rng.choice(m, min(count, m), replace=False).tolist())
     return np.array(sorted(r for r in rows if 0 <= r < m), dtype=np.int64)
+
+
+# ------------------------------------------------------------------ attention
+
+def make_attention(s: int = VIDEO_TOKENS, heads: int = ATTN_HEADS, seed: int = ATTN_SEED,
+                   qk_std: float = 2.0, k_outlier: float = 0.0) -> dict:
+    """Inputs of the attention: one fused QKV matrix, raw bf16 [s, 3 * heads *
+    128] with Q, K, V in that order along the columns and head h at columns
+    [128 h, 128 h + 128) of each third.
+
+    Synthetic statistics (the pages give none for attention): Q and K are
+    N(0, qk_std^2), so the logits q.k / sqrt(128) have standard deviation
+    qk_std^2 (4 by default: peaked, not one-hot, over 32256 keys); V is
+    N(0, 1).  ``k_outlier`` > 0 multiplies one seeded channel of every key
+    head by that factor (a shared key offset direction that makes the
+    per-token key scales coarse).  Draw order: Q, K, V, then the outlier
+    channels."""
+    rng = np.random.default_rng(seed)
+    w = heads * ATTN_HEAD_DIM
+    qkv = np.empty((s, 3 * w), np.float32)
+    qkv[:, :w] = _normal(rng, (s, w), qk_std)
+    qkv[:, w:2 * w] = _normal(rng, (s, w), qk_std)
+    qkv[:, 2 * w:] = _normal(rng, (s, w))
+    if k_outlier > 0:
+        ch = rng.integers(0, ATTN_HEAD_DIM, size=heads)
+        cols = w + np.arange(heads) * ATTN_HEAD_DIM + ch
+        qkv[:, cols] *= np.float32(k_outlier)
+    return {"qkv": to_bf16_bits(qkv), "s": s, "heads": heads}
