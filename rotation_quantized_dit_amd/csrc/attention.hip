@@ -17,7 +17,7 @@
 //          MFMA operand here.  K, its scales and V are padded to a multiple of
 //          64 keys with zeros (masked in the softmax).
 //   flash: one workgroup of 8 waves owns 256 queries of one head, 32 per
-//          wave; K, V^T and the key scales stream through a 4-slot LDS ring
+//          wave; K, V^T and the key scales stream through a 5-slot LDS ring
 //          in blocks of 64 keys (25 KiB per slot), copied with the direct
 //          buffer loads into LDS.
 //
@@ -58,7 +58,7 @@ constexpr int QW = 32;                  // queries per wave
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int QB = QW * NWAVES;         // queries per workgroup
-constexpr int STAGES = 4;
+constexpr int STAGES = 5;
 constexpr int K_BYTES = KB * D;         // int8 key codes of a block
 constexpr int V_BYTES = KB * D * 2;     // fp16 V^T of a block
 constexpr int S_BYTES = KB * 4;         // key scales of a block
@@ -75,6 +75,16 @@ typedef float v16f __attribute__((ext_vector_type(16)));
 typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) const v4i lds_v4i;
+typedef __attribute__((address_space(3))) const v4f lds_v4f;
+typedef __attribute__((address_space(3))) const v8h lds_v8h;
+typedef __attribute__((address_space(3))) const uint8_t lds_u8;
+
+// 32-bit LDS address of a pointer into shared memory, and back.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(lds_u8*)p;
+}
+__device__ __forceinline__ lds_u8* lds_ptr(uint32_t a) { return (lds_u8*)(uintptr_t)a; }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -109,6 +119,12 @@ __device__ __forceinline__ void copy4(__amdgpu_buffer_rsrc_t rsrc, uint8_t* dst,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 4, voff, soff, 0, 0);
 #endif
 }
+
+// LDS rows of K and V^T are 128 bytes (8 chunks of 16); chunk c of row r is
+// stored at c ^ swz(r).  A 16-byte read by 16 lanes spans 256 bytes of banks,
+// so rows r and r + 2 k must differ in chunk for the 16 rows a fragment read
+// touches: (r / 2) % 8 does that (r % 8 would pair rows r and r + 8).
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 // Position of key j inside its 32-key block in V^T: bits 2 and 3 swapped.
 __device__ __forceinline__ int vt_pos(int j) {
@@ -228,67 +244,61 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_flash_kernel(
     const int nb = S_pad / KB;
 
     // This lane's query: codes as the B operand of the four 32-byte d-steps
-    // (bytes 16 (2 s + g) .. +15), and c = s_q log2(e) / sqrt(d).
+    // (bytes 16 (2 s + g) .. +15), and c = s_q log2(e) / sqrt(d).  An
+    // all-zero query (s_q = 0) has all-zero codes, so every logit of its row
+    // is 0 whatever c is; c = 1 there keeps -inf * c = -inf for masked keys.
     const int qi = q0 + QW * wave + l31;
     const int qr = qi < S ? qi : S - 1;
     const int8_t* qrow = qc + ((int64_t)h * S + qr) * D;
     v4i qf[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) qf[s] = *reinterpret_cast<const v4i*>(qrow + 16 * (2 * s + g));
-    const float c = sq[(int64_t)h * S + qr] * c_log2;
+    const float c_raw = sq[(int64_t)h * S + qr] * c_log2;
+    const float c = c_raw > 0.0f ? c_raw : 1.0f;
 
     // Copy sources (per head): K block rows 8 w + l / 8, V^T block rows
     // 16 w + 8 i + l / 8; lane l lands at chunk position l % 8 of its row,
-    // which holds logical chunk (l % 8) ^ (row % 8).
+    // which holds logical chunk (l % 8) ^ swz(row).
     const __amdgpu_buffer_rsrc_t rk = make_rsrc(kc + (int64_t)h * S_pad * D, (uint32_t)S_pad * D);
     const __amdgpu_buffer_rsrc_t rv =
         make_rsrc(vt + (int64_t)h * S_pad * D, (uint32_t)S_pad * D * 2);
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(sk + (int64_t)h * S_pad, (uint32_t)S_pad * 4);
     const int kr = 8 * wave + (lane >> 3);
-    const uint32_t voff_k = (uint32_t)(kr * 128 + 16 * ((lane & 7) ^ (kr & 7)));
+    const uint32_t voff_k = (uint32_t)(kr * 128 + 16 * ((lane & 7) ^ swz(kr)));
     uint32_t voff_v[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
         const int vr = 16 * wave + 8 * i + (lane >> 3);
-        voff_v[i] = (uint32_t)(vr * 128 + 16 * ((lane & 7) ^ (vr & 7)));
+        voff_v[i] = (uint32_t)(vr * 128 + 16 * ((lane & 7) ^ swz(vr)));
     }
-    auto issue = [&](int b, int slot) {
+    auto issue = [&](int b) {
+        uint8_t* st = lds + (b % STAGES) * STAGE_BYTES;
         b = b < nb ? b : nb - 1;         // past the end: reload the last block (unused)
-        uint8_t* st = lds + slot * STAGE_BYTES;
         copy16(rk, st + 1024 * wave, voff_k, (uint32_t)b * K_BYTES);
         copy16(rv, st + K_BYTES + 2048 * wave, voff_v[0], (uint32_t)b * V_BYTES);
         copy16(rv, st + K_BYTES + 2048 * wave + 1024, voff_v[1], (uint32_t)b * V_BYTES);
         // every wave copies the same 64 scales (identical writes)
         copy4(rs, st + K_BYTES + V_BYTES, 4u * (uint32_t)lane, (uint32_t)b * S_BYTES);
     };
+    auto slot = [&](int b) -> const uint8_t* { return lds + (b % STAGES) * STAGE_BYTES; };
 
     // Fragment byte offsets within a stage.  K: row 32 kb + l31, chunk
-    // 2 s + g; V^T: row 32 db + l31, chunk 4 kb + 2 hh + g; (row % 8) = l31 % 8.
-    const int sw = l31 & 7;
-    int k_off[2][4], v_off[4][2][2];
+    // 2 s + g; V^T: row 32 db + l31, chunk 4 kb + 2 hh + g; swz(row) = swz(l31).
+    // The 32-row block (kb for K, db for V^T) adds a constant 4096 bytes, so
+    // each lane keeps 4 + 4 offsets and the block goes into the instruction.
+    const int sw = swz(l31);
+    int k_lane[4], v_lane[4];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int s = 0; s < 4; ++s) k_lane[s] = l31 * 128 + 16 * ((2 * s + g) ^ sw);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) k_off[kb][s] = (32 * kb + l31) * 128 + 16 * ((2 * s + g) ^ sw);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                v_off[db][kb][hh] = K_BYTES + (32 * db + l31) * 128 + 16 * ((4 * kb + 2 * hh + g) ^ sw);
-
-    auto qk = [&](const uint8_t* st, v16i (&acc)[2]) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[kb][r] = 0;
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const v4i kf = *reinterpret_cast<const v4i*>(st + k_off[kb][s]);
-                acc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf, qf[s], acc[kb], 0, 0, 0);
-            }
-        }
+    for (int kh = 0; kh < 4; ++kh) v_lane[kh] = K_BYTES + l31 * 128 + 16 * ((2 * kh + g) ^ sw);
+    // K fragment (kb, s) and V^T fragment (db, kb, hh) of a stage (used
+    // outside the main loop)
+    auto kfrag = [&](const uint8_t* st, int kb, int s) -> v4i {
+        return *reinterpret_cast<const v4i*>(st + k_lane[s] + 4096 * kb);
+    };
+    auto vfrag = [&](const uint8_t* st, int db, int kb, int hh) -> v8h {
+        return *reinterpret_cast<const v8h*>(st + v_lane[2 * kb + hh] + 4096 * db);
     };
 
     v16f o[4];
@@ -297,124 +307,214 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_flash_kernel(
 #pragma unroll
         for (int r = 0; r < 16; ++r) o[db][r] = 0.0f;
     float m_ref = -__builtin_inff();
-    float lsum0 = 0.0f, lsum1 = 0.0f;
+    float lsum = 0.0f;                   // row sum of the lane's query (all keys so far)
+    const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
-    // Ring: block b lives in slot b % STAGES.  Iteration kt reads slot kt
-    // (V^T for P.V of block kt) and slot kt + 1 (K for the logits of block
-    // kt + 1), and refills slot kt - 1 with block kt + 3.
+    // S^T of a block: 2 key halves x 4 d-steps of int8 MFMA (used alone, in
+    // the prologue).
+    auto qk = [&](const uint8_t* st, v16i (&acc)[2]) {
 #pragma unroll
-    for (int b = 0; b < STAGES - 1; ++b) issue(b, b);
-    wait_vmcnt<COPIES>();
-    lds_barrier();
-    v16i sacc[2], snext[2];
-    qk(lds, sacc);
-
-    for (int kt = 0; kt < nb; ++kt) {
-        wait_vmcnt<COPIES>();            // block kt + 1 has landed
-        lds_barrier();                   // ... for every wave; slot kt - 1 is free
-        issue(kt + STAGES - 1, (kt + STAGES - 1) % STAGES);
-        const uint8_t* cur = lds + (kt % STAGES) * STAGE_BYTES;
-        const uint8_t* nxt = lds + ((kt + 1) % STAGES) * STAGE_BYTES;
-
-        // logits of the next block (independent of this block's softmax)
-        qk(nxt, snext);
-
-        // t = acc * s_k for this lane's 32 keys of the block
-        float t[2][16];
+        for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+            for (int r = 0; r < 16; ++r) acc[kb][r] = 0;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const v4f skv = *reinterpret_cast<const v4f*>(cur + K_BYTES + V_BYTES +
-                                                              4 * (32 * kb + 8 * j + 4 * g));
-#pragma unroll
-                for (int i = 0; i < 4; ++i) t[kb][4 * j + i] = (float)sacc[kb][4 * j + i] * skv[i];
+            for (int s = 0; s < 4; ++s) {
+                acc[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kfrag(st, kb, s), qf[s], acc[kb], 0, 0, 0);
             }
-        const bool tail = (kt == nb - 1) && (S & (KB - 1)) != 0;
-        if (tail) {
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kt * KB + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (key >= S) t[kb][r] = -__builtin_inff();
-                }
         }
-        float bm = -__builtin_inff();
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; r += 2) bm = __builtin_fmaxf(bm, __builtin_fmaxf(t[kb][r], t[kb][r + 1]));
-        {
-            const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm),
-                                                              false, false);
-            bm = __builtin_fmaxf(__uint_as_float(sw2[0]), __uint_as_float(sw2[1]));
-        }
-        const float m_blk = bm * c;      // c >= 0, so this is the block's largest e + M
-        if (__builtin_amdgcn_ballot_w64(m_blk > m_ref + TAU) != 0) {
-            const float m_new = __builtin_fmaxf(m_ref, m_blk);
-            const float alpha = __builtin_amdgcn_exp2f(m_ref - m_new);
-            m_ref = m_new;
-            lsum0 *= alpha;
-            lsum1 *= alpha;
-#pragma unroll
-            for (int db = 0; db < 4; ++db)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
-        }
-        float pf[2][16];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                pf[kb][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb][r], c, -m_ref));
-        if (tail) {
-            // masked keys: with c = 0 the product -inf * c is NaN, so their
-            // probabilities are set to zero explicitly
-#pragma unroll
-            for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    const int key = kt * KB + 32 * kb + 8 * (r >> 2) + 4 * g + (r & 3);
-                    if (key >= S) pf[kb][r] = 0.0f;
-                }
-        }
-        v8h p[2][2];
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-                for (int e = 0; e < 8; e += 2) {
-                    const float p0 = pf[kb][8 * hh + e], p1 = pf[kb][8 * hh + e + 1];
-                    lsum0 += p0;
-                    lsum1 += p1;
-                    p[kb][hh][e] = (_Float16)p0;
-                    p[kb][hh][e + 1] = (_Float16)p1;
-                }
+    };
 
-        // O^T += V^T P^T
+    auto rescale = [&](float a) {
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= a;
+    };
+
+    // One pipeline step, written as the instruction stream it should become
+    // (sched_barrier fences keep each chunk together):
+    //   phase 1: the 8 MFMAs of S^T for the next block (K from st_k), each
+    //            with the conversion t = acc * s_k of 4 logits of block kc
+    //            (scales from st_s); keys past S are masked on the last block;
+    //   phase 2: the 16 MFMAs of O^T += V^T P^T for the previous block (V^T
+    //            from st_v, probabilities p_prev), each with 2 probabilities
+    //            p = 2^(t c - M) of block kc at the current reference point M
+    //            (fp16 rounding and the block's row sum);
+    //   check:   if any lane's block sum exceeds 2^TAU (or is not finite: the
+    //            first block, where M = -inf), some p may exceed 2^TAU; then
+    //            M is raised to the block maximum, the block's p are computed
+    //            again, and O (which now holds the previous block too) and
+    //            the row sum are rescaled by 2^(M_old - M_new).  Otherwise no
+    //            p exceeds the sum, so every p <= 2^TAU, well inside fp16.
+    auto step = [&](int kc, const uint8_t* st_k, const uint8_t* st_s, const uint8_t* st_v, bool do_pv,
+                    const v16i (&s_cur)[2], v16i (&s_nxt)[2], const v8h (&p_prev)[2][2],
+                    v8h (&p_cur)[2][2]) {
+        // Per-step fragment base addresses (9 per lane), kept opaque so that
+        // the compiler does not re-associate them with the slot arithmetic:
+        // each read is then base + the 32-row block offset as an immediate.
+        uint32_t kbase[4], vbase[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            kbase[i] = lds_addr(st_k) + (uint32_t)k_lane[i];
+            vbase[i] = lds_addr(st_v) + (uint32_t)v_lane[i];
+            asm volatile("" : "+v"(kbase[i]));
+            asm volatile("" : "+v"(vbase[i]));
+        }
+        uint32_t sbase = lds_addr(st_s) + (uint32_t)(K_BYTES + V_BYTES + 16 * g);
+        asm volatile("" : "+v"(sbase));
+        auto kf_at = [&](int n) -> v4i {     // MFMA n of phase 1: kb = n & 1, s = n >> 1
+            return *reinterpret_cast<const lds_v4i*>(lds_ptr(kbase[n >> 1] + 4096 * (n & 1)));
+        };
+        auto sk_at = [&](int n) -> v4f {     // scales of logits 4 (n & 3) .. of half n >> 2
+            return *reinterpret_cast<const lds_v4f*>(lds_ptr(sbase + 128 * (n >> 2) + 32 * (n & 3)));
+        };
+        auto vf_at = [&](int n) -> v8h {     // MFMA n of phase 2: db = n & 3, kb = n >> 3, hh = (n >> 2) & 1
+            return *reinterpret_cast<const lds_v8h*>(
+                lds_ptr(vbase[2 * (n >> 3) + ((n >> 2) & 1)] + 4096 * (n & 3)));
+        };
+        // ---- phase 1
+        v4i kf[8];
+        v4f skv[8];
+        float t[2][16];
+        kf[0] = kf_at(0);
+        skv[0] = sk_at(0);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i + 1 < 8) {
+                kf[i + 1] = kf_at(i + 1);
+                skv[i + 1] = sk_at(i + 1);
+            }
+            {
+                const int kb = i & 1, sd = i >> 1;
+                s_nxt[kb] = __builtin_amdgcn_mfma_i32_32x32x32_i8(kf[i], qf[sd],
+                                                                  sd == 0 ? v16i{} : s_nxt[kb], 0, 0, 0);
+            }
+            const int kb = i >> 2, j = i & 3;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) t[kb][4 * j + e] = (float)s_cur[kb][4 * j + e] * skv[i][e];
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (kc == nb - 1) {
+            const int nvalid = S - kc * KB;          // 1 .. 64
+#pragma unroll
             for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-                for (int hh = 0; hh < 2; ++hh) {
-                    const v8h vf = *reinterpret_cast<const v8h*>(cur + v_off[db][kb][hh]);
-                    o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, p[kb][hh], o[db], 0, 0, 0);
-                }
+                for (int r = 0; r < 16; ++r)
+                    if (32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) >= nvalid) t[kb][r] = -__builtin_inff();
+        }
+        // ---- phase 2
+        constexpr int VD = 4;                        // V^T fragment prefetch distance
+        v8h vf[16];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) sacc[kb] = snext[kb];
-    }
+        for (int i = 0; i < VD; ++i) vf[i] = vf_at(i);
+        float bs0 = 0.0f, bs1 = 0.0f;
+        // p for logits r, r + 1 of half kb, packed into p_cur, summed into bs
+        auto prob2 = [&](int kb, int r, float m, float& bs) {
+            const float p0 = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb][r], c, -m));
+            const float p1 = __builtin_amdgcn_exp2f(__builtin_fmaf(t[kb][r + 1], c, -m));
+            // (the block sum consumes the pair in this basic block, which keeps
+            // the pair here rather than sunk to its use in the next step)
+            const h2 pp = {(_Float16)p0, (_Float16)p1};
+            p_cur[kb][r >> 3][r & 7] = pp[0];
+            p_cur[kb][r >> 3][(r & 7) + 1] = pp[1];
+            bs = __builtin_amdgcn_fdot2(pp, ones, bs, false);
+        };
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            if (i + VD < 16) vf[i + VD] = vf_at(i + VD);
+            if (do_pv) {
+                const int db = i & 3, kb = i >> 3, hh = (i >> 2) & 1;
+                o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf[i], p_prev[kb][hh], o[db], 0, 0, 0);
+            }
+            if (i & 1)
+                prob2(i >> 3, 2 * (i & 7), m_ref, bs1);
+            else
+                prob2(i >> 3, 2 * (i & 7), m_ref, bs0);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // ---- check (bs: the block's row sum over both lane halves' keys)
+        auto both_halves = [](float x) {
+            const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+            return __uint_as_float(w[0]) + __uint_as_float(w[1]);
+        };
+        float bs = both_halves(bs0 + bs1);
+        if (__builtin_amdgcn_ballot_w64(!(bs <= 256.0f)) != 0) {
+            float mx0 = __builtin_fmaxf(t[0][0], t[0][1]);
+            float mx1 = __builtin_fmaxf(t[1][0], t[1][1]);
+#pragma unroll
+            for (int r = 2; r < 16; r += 2) {
+                mx0 = __builtin_fmaxf(mx0, __builtin_fmaxf(t[0][r], t[0][r + 1]));
+                mx1 = __builtin_fmaxf(mx1, __builtin_fmaxf(t[1][r], t[1][r + 1]));
+            }
+            float bm = __builtin_fmaxf(mx0, mx1);
+            const auto w = __builtin_amdgcn_permlane32_swap(__float_as_uint(bm), __float_as_uint(bm), false,
+                                                            false);
+            bm = __builtin_fmaxf(__uint_as_float(w[0]), __uint_as_float(w[1]));
+            const float m_new = __builtin_fmaxf(m_ref, bm * c);   // c > 0
+            const float a = __builtin_amdgcn_exp2f(m_ref - m_new);
+            m_ref = m_new;
+            bs0 = 0.0f;
+            bs1 = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                if (i & 1)
+                    prob2(i >> 3, 2 * (i & 7), m_ref, bs1);
+                else
+                    prob2(i >> 3, 2 * (i & 7), m_ref, bs0);
+            }
+            lsum *= a;
+            if (do_pv) rescale(a);
+            bs = both_halves(bs0 + bs1);
+        }
+        lsum += bs;
+    };
+    // O^T += V^T P^T for one block, alone (the last block).
+    auto pv = [&](const uint8_t* st, const v8h (&p)[2][2]) {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int db = i & 3, kb = i >> 3, hh = (i >> 2) & 1;
+            o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vfrag(st, db, kb, hh), p[kb][hh], o[db], 0, 0, 0);
+        }
+    };
 
-    // Row sum over both lane halves, then O / l in bf16: lane holds head dims
-    // 32 db + 8 j + 4 g + i (i = 0..3) of its query.
-    float lsum = lsum0 + lsum1;
-    {
-        const auto sw2 = __builtin_amdgcn_permlane32_swap(__float_as_uint(lsum), __float_as_uint(lsum),
-                                                          false, false);
-        lsum = __uint_as_float(sw2[0]) + __uint_as_float(sw2[1]);
+    // Ring of STAGES slots, block b in slot b % STAGES.  Iteration kt reads
+    // slot kt - 1 (V^T for P.V of block kt - 1), slot kt (key scales for the
+    // softmax of block kt) and slot kt + 1 (K for the logits of block kt + 1)
+    // while blocks kt + 2 and kt + 3 are in flight.
+    auto iter = [&](int kt, const v16i (&s_cur)[2], v16i (&s_nxt)[2], const v8h (&p_prev)[2][2],
+                    v8h (&p_cur)[2][2]) {
+        wait_vmcnt<COPIES>();            // block kt + 1 has landed
+        lds_barrier();                   // ... for every wave; slot kt - 2 is free
+        issue(kt + 3);
+        step(kt, slot(kt + 1), slot(kt), slot(kt + STAGES - 1), kt > 0, s_cur, s_nxt, p_prev, p_cur);
+    };
+
+    v16i sa[2], sb[2];
+    v8h pa[2][2], pb[2][2];
+    issue(0);
+    issue(1);
+    issue(2);
+    wait_vmcnt<2 * COPIES>();            // block 0 has landed
+    lds_barrier();
+    qk(slot(0), sa);
+    // Iterations 0 .. nb - 1; registers alternate between the (a) and (b)
+    // sets, two iterations per loop trip.
+    iter(0, sa, sb, pb, pa);
+    int kt = 1;
+    for (; kt + 1 < nb; kt += 2) {
+        iter(kt, sb, sa, pa, pb);
+        iter(kt + 1, sa, sb, pb, pa);
     }
+    if (kt < nb) {                       // one iteration left (kt = nb - 1)
+        iter(kt, sb, sa, pa, pb);
+        pv(slot(nb - 1), pb);
+    } else {
+        pv(slot(nb - 1), pa);
+    }
+    wait_vmcnt<0>();                     // the trailing (unused) copies
+
+    // O / l in bf16 (lsum already holds both lane halves' keys): lane holds
+    // head dims 32 db + 8 j + 4 g + i (i = 0..3) of its query.
     if (qi < S) {
         const float inv = 1.0f / lsum;
         uint16_t* orow = out + (int64_t)qi * ld_out + h * D;

@@ -175,3 +175,36 @@ def test_attention_validation(cr):
     ws = torch.empty(16, dtype=torch.uint8, device="cuda")
     with pytest.raises(cr.ConvRotError):
         cr.attention(x[:, :w], x[:, w:2 * w], x[:, 2 * w:], heads, workspace=ws)
+
+
+def test_attention_full_size(cr):
+    """The benchmark's configuration, 32256 tokens x 42 heads of 128, one call
+    of each entry point: Q/K codes and scales of every token and head bit for
+    bit, the V layout of every head, and the output of sampled queries (first,
+    last, 24 seeded) of heads 0, 21 and 41 against all 32256 keys."""
+    import torch
+    s, heads = workloads.VIDEO_TOKENS, workloads.ATTN_HEADS
+    print("attention full size: generating %d x %d" % (s, 3 * heads * D), flush=True)
+    a = workloads.make_attention()
+    qkv = gu.dev_bf16(a["qkv"])
+    w = heads * D
+    ws = cr.attention_prep(qkv[:, :w], qkv[:, w:2 * w], qkv[:, 2 * w:], heads)
+    out = cr.attention_prepared(ws, s, heads)
+    torch.cuda.synchronize()
+    out_h, ws_h = gu.host_bf16(out), gu.host(ws)
+    del qkv, ws, out
+    print("attention full size: oracle codes", flush=True)
+    q, k, v = thirds(a["qkv"], heads)
+    qh, kh = oracle.split_heads(q, heads), oracle.split_heads(k, heads)
+    qc, sq = oracle.attention_quant(qh.reshape(-1, D))
+    kc, sk = oracle.attention_quant(kh.reshape(-1, D))
+    codes = (qc.reshape(heads, s, D), sq.reshape(heads, s), kc.reshape(heads, s, D), sk.reshape(heads, s))
+    check_workspace(ws_h, a["qkv"], heads, codes, "full size")
+    rows = workloads.sample_rows(s, seed=workloads.ATTN_SEED, count=24)
+    vh = oracle.split_heads(v, heads)
+    for h in (0, 21, 41):
+        print("attention full size: oracle head %d, %d queries" % (h, rows.size), flush=True)
+        ref, absw = oracle.attention_rows(codes[0][h][rows], codes[1][h][rows], codes[2][h], codes[3][h],
+                                          oracle.to_fp16(vh[h]))
+        sub = out_h[:, h * D:(h + 1) * D]
+        assert_attn_close(sub, ref[None], absw[None], 1, rows, "full size head %d" % h)

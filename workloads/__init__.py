@@ -194,12 +194,13 @@ def make_attention(s: int = VIDEO_TOKENS, heads: int = ATTN_HEADS, seed: int = A
     channels."""
     rng = np.random.default_rng(seed)
     w = heads * ATTN_HEAD_DIM
-    qkv = np.empty((s, 3 * w), np.float32)
-    qkv[:, :w] = _normal(rng, (s, w), qk_std)
-    qkv[:, w:2 * w] = _normal(rng, (s, w), qk_std)
-    qkv[:, 2 * w:] = _normal(rng, (s, w))
+    q = _normal(rng, (s, w), qk_std)
+    k = _normal(rng, (s, w), qk_std)
+    v = _normal(rng, (s, w))
     if k_outlier > 0:
         ch = rng.integers(0, ATTN_HEAD_DIM, size=heads)
-        cols = w + np.arange(heads) * ATTN_HEAD_DIM + ch
-        qkv[:, cols] *= np.float32(k_outlier)
-    return {"qkv": to_bf16_bits(qkv), "s": s, "heads": heads}
+        k[:, np.arange(heads) * ATTN_HEAD_DIM + ch] *= np.float32(k_outlier)
+    bits = np.empty((s, 3 * w), np.uint16)
+    for i, t in enumerate((q, k, v)):
+        bits[:, i * w:(i + 1) * w] = to_bf16_bits(t)
+    return {"qkv": bits, "s": s, "heads": heads}
