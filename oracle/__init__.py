@@ -77,6 +77,9 @@ def lib() -> ctypes.CDLL:
         L.orc_dequantize_weight.argtypes = [P, P, I64, I64, P]
         L.orc_lora_add.argtypes = [P, I64, I64, P, P, I64, ctypes.c_float]
         L.orc_attention_rows.argtypes = [P, P, I64, P, P, P, I64, I64, P, P]
+        L.orc_mx_quantize_rows.argtypes = [P, I64, I64, P, P]
+        L.orc_mx_decode.argtypes = [P, P, I64, I64, P]
+        L.orc_mx_gemm.argtypes = [P, P, I64, P, P, I64, I64, P, P]
         _lib = L
     return _lib
 
@@ -364,3 +367,46 @@ def attention(q_bf16, k_bf16, v_bf16, heads: int, rows=None):
         qcs.append(qc); sqs.append(sq); kcs.append(kc); sks.append(sk)
     return (np.stack(outs), np.stack(absws),
             (np.stack(qcs), np.stack(sqs), np.stack(kcs), np.stack(sks)))
+
+
+# ------------------------------------------------------------------ MXFP4
+
+def mx_quantize(v: np.ndarray):
+    """fp32 rows [r, k] (k % 32 == 0) -> (FP4 E2M1 codes packed two per byte
+    [r, k/2] uint8, E8M0 block scales [r, k/32] uint8)."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    r, k = v.shape
+    assert k % 32 == 0
+    codes = np.zeros((r, k // 2), np.uint8)
+    scales = np.zeros((r, k // 32), np.uint8)
+    lib().orc_mx_quantize_rows(_p(v), r, k, _p(codes), _p(scales))
+    return codes, scales
+
+
+def mx_quantize_act(x_bf16: np.ndarray):
+    """MXFP4 of bf16 activation rows (widened exactly)."""
+    return mx_quantize(bf16_to_f32(x_bf16))
+
+
+def mx_decode(codes: np.ndarray, scales: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint8)
+    r, k2 = codes.shape
+    out = np.empty((r, 2 * k2), np.float64)
+    lib().orc_mx_decode(_p(codes), _p(scales), r, 2 * k2, _p(out))
+    return out
+
+
+def mx_gemm(ac, asc, bc, bsc):
+    """fp64 y = A B^T of two MXFP4 matrices, and sum |a b| per output."""
+    ac = np.ascontiguousarray(ac, dtype=np.uint8)
+    asc = np.ascontiguousarray(asc, dtype=np.uint8)
+    bc = np.ascontiguousarray(bc, dtype=np.uint8)
+    bsc = np.ascontiguousarray(bsc, dtype=np.uint8)
+    m, k2 = ac.shape
+    n = bc.shape[0]
+    assert bc.shape[1] == k2 and asc.shape == (m, k2 // 16) and bsc.shape == (n, k2 // 16)
+    y = np.empty((m, n), np.float64)
+    absacc = np.empty((m, n), np.float64)
+    lib().orc_mx_gemm(_p(ac), _p(asc), m, _p(bc), _p(bsc), n, 2 * k2, _p(y), _p(absacc))
+    return y, absacc

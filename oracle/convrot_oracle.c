@@ -460,3 +460,114 @@ void orc_attention_rows(const int8_t* qc, const float* sq, int64_t nq, const int
         free(logit);
     }
 }
+
+/* ------------------------------------------------------- MXFP4 (NEXT row)
+ *
+ * The hybrid checkpoints of the Minimax_h3_hybrid model card ("Checkpoints")
+ * run the QKV and FFN-input projections in a 4-bit block format (NVFP4) and
+ * keep the output projections int8 ConvRot.  NVFP4 is a Blackwell format;
+ * its analog on this hardware is the OCP Microscaling format MXFP4, which the
+ * MI355X matrix cores take natively.  The readings (from the OCP MX format
+ * definition, as this build reads it):
+ *   - blocks of 32 consecutive elements along K share one scale 2^e stored as
+ *     an 8-bit biased exponent (E8M0, code = e + 127);
+ *   - e = floor(log2(max |v|)) - 2 (2 is the largest exponent of the element
+ *     format), clamped to [-127, 127]; an all-zero block takes code 0;
+ *   - each element is v / 2^e (exact: a power-of-two scaling) rounded to
+ *     FP4 E2M1 (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6), to nearest, ties to
+ *     the even mantissa bit, magnitudes above 6 saturated to 6; the sign bit
+ *     is the sign of v (so -0 and small negatives that round to zero keep it);
+ *   - element 2j of a row is the low nibble of byte j, element 2j + 1 the high
+ *     nibble; no rotation (the hybrid's NVFP4 layers carry none). */
+
+/* E2M1 magnitude of a 3-bit code (exponent bits 2..1, mantissa bit 0). */
+static double e2m1_mag(int c) {
+    const int e = (c >> 1) & 3, m = c & 1;
+    return e == 0 ? 0.5 * m : ldexp(1.0 + 0.5 * m, e - 1);
+}
+
+/* Nearest E2M1 magnitude code of y >= 0: the candidates are taken in order;
+ * at an exact midpoint the code with mantissa bit 0 wins; above 6 saturates. */
+static int e2m1_round(double y) {
+    if (y >= 6.0) return 7;
+    int best = 0;
+    double bd = y;                      /* distance to code 0 (magnitude 0) */
+    for (int c = 1; c < 8; ++c) {
+        const double d = fabs(y - e2m1_mag(c));
+        if (d < bd || (d == bd && (c & 1) == 0)) {
+            best = c;
+            bd = d;
+        }
+    }
+    return best;
+}
+
+void orc_mx_quantize_rows(const float* v, int64_t rows, int64_t k, uint8_t* codes, uint8_t* scales) {
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r) {
+        for (int64_t b = 0; b < k / 32; ++b) {
+            const float* x = v + r * k + 32 * b;
+            float amax = 0.0f;
+            for (int i = 0; i < 32; ++i)
+                if (fabsf(x[i]) > amax) amax = fabsf(x[i]);
+            int e = -127;
+            if (amax > 0.0f) {
+                int fe;
+                frexpf(amax, &fe);     /* amax = f 2^fe, f in [0.5, 1): floor(log2) = fe - 1 */
+                e = fe - 1 - 2;
+                if (e < -127) e = -127;
+                if (e > 127) e = 127;
+            }
+            scales[r * (k / 32) + b] = (uint8_t)(e + 127);
+            for (int i = 0; i < 32; ++i) {
+                const double y = ldexp((double)x[i], -e);
+                const int c = (signbit(x[i]) ? 8 : 0) | (amax > 0.0f ? e2m1_round(fabs(y)) : 0);
+                uint8_t* byte = codes + r * (k / 2) + 16 * b + i / 2;
+                if (i % 2 == 0)
+                    *byte = (uint8_t)((*byte & 0xf0) | c);
+                else
+                    *byte = (uint8_t)((*byte & 0x0f) | (c << 4));
+            }
+        }
+    }
+}
+
+/* Value of element i of a quantized row. */
+static double mx_value(const uint8_t* codes, const uint8_t* scales, int64_t i) {
+    const int c = (i % 2 == 0) ? (codes[i / 2] & 15) : (codes[i / 2] >> 4);
+    const double m = e2m1_mag(c & 7);
+    return ldexp((c & 8) ? -m : m, (int)scales[i / 32] - 127);
+}
+
+void orc_mx_decode(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t k, double* out) {
+    int64_t r;
+#pragma omp parallel for schedule(static)
+    for (r = 0; r < rows; ++r)
+        for (int64_t i = 0; i < k; ++i)
+            out[r * k + i] = mx_value(codes + r * (k / 2), scales + r * (k / 32), i);
+}
+
+/* y[m][n] = sum_k a[m][k] b[n][k] over the decoded values, in fp64 (exact for
+ * these operands: every product is a short binary fraction); absacc receives
+ * sum_k |a b| (the scale of the fp32 accumulation error of a kernel). */
+void orc_mx_gemm(const uint8_t* ac, const uint8_t* as, int64_t m, const uint8_t* bc, const uint8_t* bs,
+                 int64_t n, int64_t k, double* y, double* absacc) {
+    int64_t r;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (r = 0; r < m; ++r) {
+        double* arow = (double*)malloc((size_t)k * sizeof(double));
+        for (int64_t i = 0; i < k; ++i) arow[i] = mx_value(ac + r * (k / 2), as + r * (k / 32), i);
+        for (int64_t c = 0; c < n; ++c) {
+            double s = 0.0, sa = 0.0;
+            for (int64_t i = 0; i < k; ++i) {
+                const double p = arow[i] * mx_value(bc + c * (k / 2), bs + c * (k / 32), i);
+                s += p;
+                sa += fabs(p);
+            }
+            y[r * n + c] = s;
+            absacc[r * n + c] = sa;
+        }
+        free(arow);
+    }
+}

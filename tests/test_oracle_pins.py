@@ -825,3 +825,120 @@ def test_attention_quant_is_the_per_row_quantizer():
             t = Fraction(float(f[r, c])) / Fraction(float(s[r]))
             n = round(t)          # Python rounds exact halves to even
             assert q[r, c] == max(-127, min(127, n)), (r, c)
+
+
+# ------------------------------------------------------------------ MXFP4
+
+# FP4 E2M1 magnitudes in code order (code = exponent bits 2..1, mantissa bit 0),
+# as the OCP Microscaling format lists them.
+E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def _nibbles(codes):
+    lo, hi = codes & 15, codes >> 4
+    return np.stack([lo, hi], axis=-1).reshape(codes.shape[0], -1)
+
+
+def test_mx_element_values():
+    """Every one of the 16 codes decodes (with a unit scale, code 127) to the
+    listed magnitude with the sign bit's sign."""
+    codes = np.array([[(2 * j) | ((2 * j + 1) << 4) for j in range(8)] + [0] * 8], np.uint8)
+    scales = np.array([[127]], np.uint8)
+    got = oracle.mx_decode(codes, scales)[0, :16]
+    want = [E2M1[c & 7] * (-1 if c & 8 else 1) for c in range(16)]
+    assert np.array_equal(got, np.array(want))
+
+
+def test_mx_packing_hand_example():
+    """Hand-derived: a block whose largest magnitude is 6 takes scale 2^0
+    (floor(log2 6) - 2 = 0, code 127); 1.0 is code 2, -0.5 is code 9, so the
+    first byte is 0x92 (element 0 in the low nibble)."""
+    v = np.zeros((1, 32), np.float32)
+    v[0, 0], v[0, 1], v[0, 2] = 1.0, -0.5, 6.0
+    codes, scales = oracle.mx_quantize(v)
+    assert scales[0, 0] == 127
+    assert codes[0, 0] == 0x92 and codes[0, 1] == 0x07
+
+
+def test_mx_rounding_brute_force():
+    """With a block maximum of 4 (scale 2^0), every grid value y in (-8, 8)
+    (steps of 1/64, which include every midpoint) rounds to the nearest listed
+    magnitude; at a midpoint the even code wins; above 6 it saturates."""
+    ys = np.arange(-511, 512) / 64.0
+    for chunk in range(0, ys.size, 31):
+        part = ys[chunk:chunk + 31]
+        v = np.zeros((1, 32), np.float32)
+        v[0, 0] = 4.0                       # sets the scale to 2^0 (floor(log2 4) - 2 = 0) ...
+        v[0, 1:1 + part.size] = part        # ... unless a grid value reaches 8 (|y| < 8 here)
+        codes, scales = oracle.mx_quantize(v)
+        assert scales[0, 0] == 127
+        nib = _nibbles(codes)[0]
+        for j, y in enumerate(part):
+            c = int(nib[1 + j])
+            a = abs(y)
+            if a >= 6.0:
+                want = 7
+            else:
+                d = [abs(a - m) for m in E2M1]
+                best = min(d)
+                cands = [i for i in range(8) if d[i] == best]
+                want = cands[0] if len(cands) == 1 else [i for i in cands if i % 2 == 0][0]
+            assert (c & 7) == want, (y, c, want)
+            assert bool(c & 8) == bool(np.signbit(np.float32(y))), y
+
+
+def test_mx_scale_exponent_exact():
+    """For random blocks over a wide magnitude range, the scale exponent e puts
+    the block maximum in [4, 8) * 2^e (checked with exact rationals); an
+    all-zero block has code 0; exponents clamp to the E8M0 range."""
+    from fractions import Fraction
+    rng = np.random.default_rng(70)
+    v = (rng.standard_normal((64, 32)) * np.exp2(rng.integers(-40, 40, size=(64, 1)))).astype(np.float32)
+    v[5] = 0.0
+    codes, scales = oracle.mx_quantize(v)
+    for r in range(64):
+        amax = np.abs(v[r]).max()
+        if amax == 0:
+            assert scales[r, 0] == 0
+            continue
+        e = int(scales[r, 0]) - 127
+        q = Fraction(float(amax)) / Fraction(2) ** e
+        assert Fraction(4) <= q < Fraction(8), (r, e, float(q))
+    tiny = np.full((1, 32), 1e-39, np.float32)      # floor(log2) - 2 = -132 -> clamps to -127
+    _, s_t = oracle.mx_quantize(tiny)
+    assert s_t[0, 0] == 0
+
+
+def test_mx_roundtrip_bound():
+    """|v - decode(quantize(v))| <= 2^e for unsaturated elements (half the
+    widest gap, 2, between listed magnitudes) and <= 2^(e+1) for saturated
+    ones (|v| / 2^e < 8); signs agree wherever the decoded value is nonzero."""
+    rng = np.random.default_rng(71)
+    v = rng.standard_normal((50, 256)).astype(np.float32) * 3
+    codes, scales = oracle.mx_quantize(v)
+    d = oracle.mx_decode(codes, scales)
+    e = np.repeat(scales.astype(np.int64) - 127, 32, axis=1)
+    unit = np.exp2(e.astype(np.float64))
+    y = v / unit
+    err = np.abs(v - d)
+    assert np.all(err[np.abs(y) <= 6] <= unit[np.abs(y) <= 6])
+    assert np.all(err <= 2 * unit)
+    nz = d != 0
+    assert np.all(np.sign(d[nz]) == np.sign(v[nz]))
+
+
+def test_mx_gemm_against_dense():
+    """The MX product equals numpy's fp64 product of the decoded matrices
+    exactly (every product is a short binary fraction, so every partial sum
+    is exact in fp64), with A and B of different shapes (a transposed or
+    swapped operand fails); sum |a b| bounds |y|."""
+    rng = np.random.default_rng(72)
+    a = rng.standard_normal((7, 128)).astype(np.float32)
+    b = rng.standard_normal((5, 128)).astype(np.float32) * 10
+    ac, asc = oracle.mx_quantize(a)
+    bc, bsc = oracle.mx_quantize(b)
+    y, absacc = oracle.mx_gemm(ac, asc, bc, bsc)
+    ref = oracle.mx_decode(ac, asc) @ oracle.mx_decode(bc, bsc).T
+    assert np.array_equal(y, ref)
+    assert np.all(np.abs(y) <= absacc)
+    assert np.allclose(absacc, np.abs(oracle.mx_decode(ac, asc)) @ np.abs(oracle.mx_decode(bc, bsc)).T)
