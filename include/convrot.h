@@ -253,6 +253,53 @@ int convrot_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
                       int64_t heads, int64_t head_dim, uint16_t* out, int64_t ld_out,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* ------------------------------------------------------------------------
+ * MXFP4 projections: the analog, on MI355X's native microscaling format, of
+ * the hybrid checkpoints that run the QKV and FFN-input projections in a
+ * 4-bit block format while the output projections stay int8 ConvRot
+ * (Minimax_h3_hybrid model card, "Checkpoints"; its 4-bit format, NVFP4, is
+ * a different hardware's).  OCP MXFP4 as computed here:
+ *   blocks     32 consecutive elements of a row along k share one scale 2^e,
+ *              e = floor(log2(max |v|)) - 2 clamped to [-127, 127], stored as
+ *              the byte e + 127 (E8M0); an all-zero block has byte 0;
+ *   elements   v / 2^e (exact) rounded to FP4 E2M1 -- magnitudes 0, 0.5, 1,
+ *              1.5, 2, 3, 4, 6 -- to nearest, ties to the even mantissa bit,
+ *              saturating at 6; the sign bit is v's; element 2j is the low
+ *              nibble of byte j of the row's codes;
+ *   product    y[m][n] = bf16_rne(sum_k a[m][k] b[n][k]) over the decoded
+ *              values, both block scales applied inside the MFMA, fp32
+ *              accumulation (within 2^-8 |y| + (k/32) 2^-23 sum |a b| of the
+ *              exact value);
+ *   no rotation (the hybrid's 4-bit layers carry none).
+ * Layouts: codes [rows, k/2] bytes, scales [rows, k/32] bytes, row-major.
+ * k must be a positive multiple of 128, at most 2^20.  Pointers 16-byte
+ * aligned; sizes checked first; rows == 0 is a no-op.
+ * ------------------------------------------------------------------------ */
+#define CONVROT_MX_MAX_K (1 << 20)
+
+/* Quantize bf16 activation rows x [m, k] to MXFP4.                          */
+int convrot_mx_quantize_act(const uint16_t* x, int64_t m, int64_t k, uint8_t* codes, uint8_t* scales,
+                            void* stream);
+
+/* Quantize fp32 weight rows w [n, k] to MXFP4 (load time).                  */
+int convrot_mx_quantize_weight(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
+                               void* stream);
+
+/* out [m, n] bf16 = A . B^T of MXFP4 operands A [m, k] and B [n, k].        */
+int convrot_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
+                    const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, uint16_t* out,
+                    void* stream);
+
+/* Workspace convrot_mx_linear needs for m rows of k: the activation codes
+ * and scales (0 for invalid sizes).                                         */
+size_t convrot_mx_workspace_bytes(int64_t m, int64_t k);
+
+/* MXFP4 linear: quantize x [m, k] (bf16) into the workspace, then the
+ * product with the prepared weight (codes [n, k/2], scales [n, k/32]).      */
+int convrot_mx_linear(const uint16_t* x, int64_t m, int64_t k, const uint8_t* w_codes,
+                      const uint8_t* w_scales, int64_t n, uint16_t* out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
 /* Static, NUL-terminated description of a status code (never NULL).         */
 const char* convrot_status_string(int status);
 

@@ -25,6 +25,11 @@ from ._lib import (  # noqa: F401
     lora_add,
     load_library,
     merge_lora,
+    mx_gemm,
+    mx_linear,
+    mx_quantize_act,
+    mx_quantize_weight,
+    mx_workspace_bytes,
     quantize_weight,
     rotate_quant_act,
     status_string,

@@ -28,7 +28,8 @@ SYMBOLS = (
     "convrot_gemm_s32", "convrot_swiglu_rotate_quant_act", "convrot_dequantize_weight",
     "convrot_lora_add", "convrot_merge_workspace_bytes", "convrot_merge_lora", "convrot_status_string",
     "convrot_attention_workspace", "convrot_attention_prep", "convrot_attention_prepared",
-    "convrot_attention",
+    "convrot_attention", "convrot_mx_quantize_act", "convrot_mx_quantize_weight", "convrot_mx_gemm",
+    "convrot_mx_workspace_bytes", "convrot_mx_linear",
 )
 
 ATTN_HEAD_DIM = 128
@@ -74,6 +75,11 @@ def load_library() -> ctypes.CDLL:
             "convrot_attention_prep": ([P, P, P, I64, I64, I64, I64, P, SZ, P], I),
             "convrot_attention_prepared": ([P, SZ, I64, I64, I64, P, I64, P], I),
             "convrot_attention": ([P, P, P, I64, I64, I64, I64, P, I64, P, SZ, P], I),
+            "convrot_mx_quantize_act": ([P, I64, I64, P, P, P], I),
+            "convrot_mx_quantize_weight": ([P, I64, I64, P, P, P], I),
+            "convrot_mx_gemm": ([P, P, P, P, I64, I64, I64, P, P], I),
+            "convrot_mx_workspace_bytes": ([I64, I64], SZ),
+            "convrot_mx_linear": ([P, I64, I64, P, P, I64, P, P, SZ, P], I),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -389,3 +395,71 @@ def attention(q, k, v, heads: int, out=None, workspace=None):
         q.data_ptr(), k.data_ptr(), v.data_ptr(), ld, s, heads, ATTN_HEAD_DIM, o.data_ptr(),
         heads * ATTN_HEAD_DIM, ws.data_ptr(), ws.numel(), _stream()))
     return o
+
+
+# ------------------------------------------------------------------ MXFP4
+
+def _mx_outputs(rows, k, like, codes, scales):
+    codes = _out(codes, (rows, k // 2), torch.uint8, like, "codes")
+    scales = _out(scales, (rows, k // 32), torch.uint8, like, "scales")
+    return codes, scales
+
+
+def mx_quantize_act(x: torch.Tensor, codes=None, scales=None):
+    """bf16 x [m, k] -> MXFP4 (codes [m, k/2] uint8, E8M0 scales [m, k/32] uint8)."""
+    _dev(x, "x", torch.bfloat16, 2)
+    m, k = x.shape
+    codes, scales = _mx_outputs(m, k, x, codes, scales)
+    _check("convrot_mx_quantize_act", load_library().convrot_mx_quantize_act(
+        x.data_ptr(), m, k, codes.data_ptr(), scales.data_ptr(), _stream()))
+    return codes, scales
+
+
+def mx_quantize_weight(w: torch.Tensor, codes=None, scales=None):
+    """fp32 W [n, k] -> MXFP4 codes and scales (load time)."""
+    _dev(w, "w", torch.float32, 2)
+    n, k = w.shape
+    codes, scales = _mx_outputs(n, k, w, codes, scales)
+    _check("convrot_mx_quantize_weight", load_library().convrot_mx_quantize_weight(
+        w.data_ptr(), n, k, codes.data_ptr(), scales.data_ptr(), _stream()))
+    return codes, scales
+
+
+def mx_gemm(a_codes, a_scales, b_codes, b_scales, out=None):
+    """bf16 [m, n] = A . B^T of MXFP4 operands."""
+    for t, nm in ((a_codes, "a_codes"), (a_scales, "a_scales"), (b_codes, "b_codes"), (b_scales, "b_scales")):
+        _dev(t, nm, torch.uint8, 2)
+    m, k2 = a_codes.shape
+    n = b_codes.shape[0]
+    k = 2 * k2
+    if (b_codes.shape[1] != k2 or tuple(a_scales.shape) != (m, k // 32)
+            or tuple(b_scales.shape) != (n, k // 32)):
+        raise ValueError("MXFP4 operand shapes do not match")
+    y = _out(out, (m, n), torch.bfloat16, a_codes, "out")
+    _check("convrot_mx_gemm", load_library().convrot_mx_gemm(
+        a_codes.data_ptr(), a_scales.data_ptr(), b_codes.data_ptr(), b_scales.data_ptr(), m, n, k,
+        y.data_ptr(), _stream()))
+    return y
+
+
+def mx_workspace_bytes(m: int, k: int) -> int:
+    return int(load_library().convrot_mx_workspace_bytes(int(m), int(k)))
+
+
+def mx_linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, out=None, workspace=None):
+    """MXFP4 linear: bf16 x [m, k] -> bf16 y [m, n] with a prepared MXFP4 weight."""
+    _dev(x, "x", torch.bfloat16, 2)
+    _dev(w_codes, "w_codes", torch.uint8, 2)
+    _dev(w_scales, "w_scales", torch.uint8, 2)
+    m, k = x.shape
+    n = w_codes.shape[0]
+    if w_codes.shape[1] != k // 2 or tuple(w_scales.shape) != (n, k // 32):
+        raise ValueError("weight shapes do not match x %s" % (tuple(x.shape),))
+    y = _out(out, (m, n), torch.bfloat16, x, "out")
+    need = max(mx_workspace_bytes(m, k), 16)
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check("convrot_mx_linear", load_library().convrot_mx_linear(
+        x.data_ptr(), m, k, w_codes.data_ptr(), w_scales.data_ptr(), n, y.data_ptr(),
+        workspace.data_ptr(), workspace.numel(), _stream()))
+    return y

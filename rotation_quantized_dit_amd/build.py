@@ -17,7 +17,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libconvrot.so")
-SOURCES = ["convrot_api.cpp", "rotate_quant.hip", "gemm_i8.hip", "weight_ops.hip", "attention.hip"]
+SOURCES = ["convrot_api.cpp", "rotate_quant.hip", "gemm_i8.hip", "weight_ops.hip", "attention.hip", "mx_quant.hip",
+           "gemm_mx.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
