@@ -270,20 +270,26 @@ int convrot_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
  *              values, both block scales applied inside the MFMA, fp32
  *              accumulation (within 2^-8 |y| + (k/32) 2^-23 sum |a b| of the
  *              exact value);
- *   no rotation (the hybrid's 4-bit layers carry none).
+ *   rotation   optional (rotate != 0): the rows are first rotated along k
+ *              with the orthonormal Hadamard-256 exactly as the int8 ConvRot
+ *              path rotates them (k a multiple of 256), which keeps the
+ *              product of two rotated operands and spreads outlier channels
+ *              across their group; rotate == 0 is the plain format, like the
+ *              hybrid's 4-bit layers, which carry no rotation.
  * Layouts: codes [rows, k/2] bytes, scales [rows, k/32] bytes, row-major.
- * k must be a positive multiple of 128, at most 2^20.  Pointers 16-byte
- * aligned; sizes checked first; rows == 0 is a no-op.
+ * k must be a positive multiple of 128 (256 when rotating), at most 2^20.
+ * Pointers 16-byte aligned; sizes checked first; rows == 0 is a no-op.
+ * Both operands of a product must be quantized with the same rotate flag.
  * ------------------------------------------------------------------------ */
 #define CONVROT_MX_MAX_K (1 << 20)
 
-/* Quantize bf16 activation rows x [m, k] to MXFP4.                          */
-int convrot_mx_quantize_act(const uint16_t* x, int64_t m, int64_t k, uint8_t* codes, uint8_t* scales,
-                            void* stream);
+/* Quantize bf16 activation rows x [m, k] to MXFP4 (rotated if rotate).     */
+int convrot_mx_quantize_act(const uint16_t* x, int64_t m, int64_t k, int rotate, uint8_t* codes,
+                            uint8_t* scales, void* stream);
 
-/* Quantize fp32 weight rows w [n, k] to MXFP4 (load time).                  */
-int convrot_mx_quantize_weight(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
-                               void* stream);
+/* Quantize fp32 weight rows w [n, k] to MXFP4 (load time; rotated if rotate). */
+int convrot_mx_quantize_weight(const float* w, int64_t n, int64_t k, int rotate, uint8_t* codes,
+                               uint8_t* scales, void* stream);
 
 /* out [m, n] bf16 = A . B^T of MXFP4 operands A [m, k] and B [n, k].        */
 int convrot_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
@@ -294,9 +300,10 @@ int convrot_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8
  * and scales (0 for invalid sizes).                                         */
 size_t convrot_mx_workspace_bytes(int64_t m, int64_t k);
 
-/* MXFP4 linear: quantize x [m, k] (bf16) into the workspace, then the
- * product with the prepared weight (codes [n, k/2], scales [n, k/32]).      */
-int convrot_mx_linear(const uint16_t* x, int64_t m, int64_t k, const uint8_t* w_codes,
+/* MXFP4 linear: quantize x [m, k] (bf16; rotated if rotate) into the
+ * workspace, then the product with a weight prepared with the same rotate
+ * flag (codes [n, k/2], scales [n, k/32]).                                  */
+int convrot_mx_linear(const uint16_t* x, int64_t m, int64_t k, int rotate, const uint8_t* w_codes,
                       const uint8_t* w_scales, int64_t n, uint16_t* out, void* workspace,
                       size_t workspace_bytes, void* stream);
 

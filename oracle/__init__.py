@@ -410,3 +410,13 @@ def mx_gemm(ac, asc, bc, bsc):
     absacc = np.empty((m, n), np.float64)
     lib().orc_mx_gemm(_p(ac), _p(asc), m, _p(bc), _p(bsc), n, 2 * k2, _p(y), _p(absacc))
     return y, absacc
+
+
+def mx_quantize_rotated(v: np.ndarray):
+    """MXFP4 of fp32 rows after the orthonormal Hadamard-256 rotation of the
+    int8 ConvRot path (the pinned rotation, then the pinned MX quantizer)."""
+    return mx_quantize(rotate_rows(np.ascontiguousarray(v, dtype=np.float32)))
+
+
+def mx_quantize_act_rotated(x_bf16: np.ndarray):
+    return mx_quantize_rotated(bf16_to_f32(x_bf16))

@@ -75,11 +75,11 @@ def load_library() -> ctypes.CDLL:
             "convrot_attention_prep": ([P, P, P, I64, I64, I64, I64, P, SZ, P], I),
             "convrot_attention_prepared": ([P, SZ, I64, I64, I64, P, I64, P], I),
             "convrot_attention": ([P, P, P, I64, I64, I64, I64, P, I64, P, SZ, P], I),
-            "convrot_mx_quantize_act": ([P, I64, I64, P, P, P], I),
-            "convrot_mx_quantize_weight": ([P, I64, I64, P, P, P], I),
+            "convrot_mx_quantize_act": ([P, I64, I64, I, P, P, P], I),
+            "convrot_mx_quantize_weight": ([P, I64, I64, I, P, P, P], I),
             "convrot_mx_gemm": ([P, P, P, P, I64, I64, I64, P, P], I),
             "convrot_mx_workspace_bytes": ([I64, I64], SZ),
-            "convrot_mx_linear": ([P, I64, I64, P, P, I64, P, P, SZ, P], I),
+            "convrot_mx_linear": ([P, I64, I64, I, P, P, I64, P, P, SZ, P], I),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -405,23 +405,24 @@ def _mx_outputs(rows, k, like, codes, scales):
     return codes, scales
 
 
-def mx_quantize_act(x: torch.Tensor, codes=None, scales=None):
-    """bf16 x [m, k] -> MXFP4 (codes [m, k/2] uint8, E8M0 scales [m, k/32] uint8)."""
+def mx_quantize_act(x: torch.Tensor, codes=None, scales=None, rotate=False):
+    """bf16 x [m, k] -> MXFP4 (codes [m, k/2] uint8, E8M0 scales [m, k/32] uint8),
+    of the Hadamard-256-rotated rows if ``rotate``."""
     _dev(x, "x", torch.bfloat16, 2)
     m, k = x.shape
     codes, scales = _mx_outputs(m, k, x, codes, scales)
     _check("convrot_mx_quantize_act", load_library().convrot_mx_quantize_act(
-        x.data_ptr(), m, k, codes.data_ptr(), scales.data_ptr(), _stream()))
+        x.data_ptr(), m, k, int(bool(rotate)), codes.data_ptr(), scales.data_ptr(), _stream()))
     return codes, scales
 
 
-def mx_quantize_weight(w: torch.Tensor, codes=None, scales=None):
-    """fp32 W [n, k] -> MXFP4 codes and scales (load time)."""
+def mx_quantize_weight(w: torch.Tensor, codes=None, scales=None, rotate=False):
+    """fp32 W [n, k] -> MXFP4 codes and scales (load time), rotated if ``rotate``."""
     _dev(w, "w", torch.float32, 2)
     n, k = w.shape
     codes, scales = _mx_outputs(n, k, w, codes, scales)
     _check("convrot_mx_quantize_weight", load_library().convrot_mx_quantize_weight(
-        w.data_ptr(), n, k, codes.data_ptr(), scales.data_ptr(), _stream()))
+        w.data_ptr(), n, k, int(bool(rotate)), codes.data_ptr(), scales.data_ptr(), _stream()))
     return codes, scales
 
 
@@ -446,8 +447,10 @@ def mx_workspace_bytes(m: int, k: int) -> int:
     return int(load_library().convrot_mx_workspace_bytes(int(m), int(k)))
 
 
-def mx_linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, out=None, workspace=None):
-    """MXFP4 linear: bf16 x [m, k] -> bf16 y [m, n] with a prepared MXFP4 weight."""
+def mx_linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, out=None, workspace=None,
+              rotate=False):
+    """MXFP4 linear: bf16 x [m, k] -> bf16 y [m, n] with an MXFP4 weight prepared
+    with the same ``rotate`` flag."""
     _dev(x, "x", torch.bfloat16, 2)
     _dev(w_codes, "w_codes", torch.uint8, 2)
     _dev(w_scales, "w_scales", torch.uint8, 2)
@@ -460,6 +463,6 @@ def mx_linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, ou
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
     _check("convrot_mx_linear", load_library().convrot_mx_linear(
-        x.data_ptr(), m, k, w_codes.data_ptr(), w_scales.data_ptr(), n, y.data_ptr(),
+        x.data_ptr(), m, k, int(bool(rotate)), w_codes.data_ptr(), w_scales.data_ptr(), n, y.data_ptr(),
         workspace.data_ptr(), workspace.numel(), _stream()))
     return y

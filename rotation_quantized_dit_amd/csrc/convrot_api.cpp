@@ -327,12 +327,13 @@ int convrot_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
 
 namespace {
 
-int check_mx_k(int64_t k) {
-    if (k <= 0 || (k % 128) != 0 || k > CONVROT_MX_MAX_K) return CONVROT_ERR_SHAPE;
+int check_mx_k(int64_t k, int rotate = 0) {
+    if (k <= 0 || (k % (rotate ? 256 : 128)) != 0 || k > CONVROT_MX_MAX_K) return CONVROT_ERR_SHAPE;
     return CONVROT_OK;
 }
 
 int check_mx_rows(int64_t r, int64_t k) {
+    // (the rotated pass launches r * k / 4096 workgroups, fewer than the plain one)
     if (r < 0 || r > (int64_t)INT32_MAX) return CONVROT_ERR_SHAPE;
     if (r * (k / 8) > (int64_t)INT32_MAX * 256) return CONVROT_ERR_SHAPE;   // quantize grid
     return CONVROT_OK;
@@ -344,24 +345,24 @@ size_t mx_scales_offset(int64_t m, int64_t k) { return ((size_t)m * (size_t)(k /
 
 extern "C" {
 
-int convrot_mx_quantize_act(const uint16_t* x, int64_t m, int64_t k, uint8_t* codes, uint8_t* scales,
-                            void* stream) {
-    if (int st = check_mx_k(k)) return st;
+int convrot_mx_quantize_act(const uint16_t* x, int64_t m, int64_t k, int rotate, uint8_t* codes,
+                            uint8_t* scales, void* stream) {
+    if (int st = check_mx_k(k, rotate)) return st;
     if (int st = check_mx_rows(m, k)) return st;
     if (m == 0) return CONVROT_OK;
     if (!x || !codes || !scales) return CONVROT_ERR_NULL;
     if (!aligned16(x) || !aligned16(codes) || !aligned16(scales)) return CONVROT_ERR_ALIGN;
-    return launched(convrot::launch_mx_quant_bf16(x, m, k, codes, scales, (hipStream_t)stream));
+    return launched(convrot::launch_mx_quant_bf16(x, m, k, rotate != 0, codes, scales, (hipStream_t)stream));
 }
 
-int convrot_mx_quantize_weight(const float* w, int64_t n, int64_t k, uint8_t* codes, uint8_t* scales,
-                               void* stream) {
-    if (int st = check_mx_k(k)) return st;
+int convrot_mx_quantize_weight(const float* w, int64_t n, int64_t k, int rotate, uint8_t* codes,
+                               uint8_t* scales, void* stream) {
+    if (int st = check_mx_k(k, rotate)) return st;
     if (int st = check_mx_rows(n, k)) return st;
     if (n == 0) return CONVROT_OK;
     if (!w || !codes || !scales) return CONVROT_ERR_NULL;
     if (!aligned16(w) || !aligned16(codes) || !aligned16(scales)) return CONVROT_ERR_ALIGN;
-    return launched(convrot::launch_mx_quant_f32(w, n, k, codes, scales, (hipStream_t)stream));
+    return launched(convrot::launch_mx_quant_f32(w, n, k, rotate != 0, codes, scales, (hipStream_t)stream));
 }
 
 int convrot_mx_gemm(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
@@ -386,10 +387,10 @@ size_t convrot_mx_workspace_bytes(int64_t m, int64_t k) {
     return mx_scales_offset(m, k) + (size_t)m * (size_t)(k / 32);
 }
 
-int convrot_mx_linear(const uint16_t* x, int64_t m, int64_t k, const uint8_t* w_codes,
+int convrot_mx_linear(const uint16_t* x, int64_t m, int64_t k, int rotate, const uint8_t* w_codes,
                       const uint8_t* w_scales, int64_t n, uint16_t* out, void* workspace,
                       size_t workspace_bytes, void* stream) {
-    if (int st = check_mx_k(k)) return st;
+    if (int st = check_mx_k(k, rotate)) return st;
     if (int st = check_mx_rows(m, k)) return st;
     if (n < 0 || n > (int64_t)INT32_MAX) return CONVROT_ERR_SHAPE;
     if (((m + 255) / 256) * ((n + 255) / 256) > (int64_t)INT32_MAX) return CONVROT_ERR_SHAPE;
@@ -403,7 +404,8 @@ int convrot_mx_linear(const uint16_t* x, int64_t m, int64_t k, const uint8_t* w_
     uint8_t* codes = (uint8_t*)workspace;
     uint8_t* scales = codes + mx_scales_offset(m, k);
     hipStream_t s = (hipStream_t)stream;
-    if (convrot::launch_mx_quant_bf16(x, m, k, codes, scales, s) != hipSuccess) return CONVROT_ERR_LAUNCH;
+    if (convrot::launch_mx_quant_bf16(x, m, k, rotate != 0, codes, scales, s) != hipSuccess)
+        return CONVROT_ERR_LAUNCH;
     return launched(convrot::launch_gemm_mx(codes, scales, w_codes, w_scales, m, n, k, out, s));
 }
 

@@ -46,11 +46,13 @@ hipError_t launch_attn_flash(const int8_t* qc, const float* sq, const int8_t* kc
                              hipStream_t stream);
 
 // MXFP4: block-32 E8M0 scales + FP4 E2M1 codes (two per byte) of rows of k
-// elements (k % 128 == 0): codes [rows, k/2], scales [rows, k/32].
-hipError_t launch_mx_quant_bf16(const uint16_t* x, int64_t rows, int64_t k, uint8_t* codes,
+// elements (k % 128 == 0; with rotate, k % 256 == 0 and the rows are first
+// rotated by the Hadamard-256 of the int8 path): codes [rows, k/2], scales
+// [rows, k/32].
+hipError_t launch_mx_quant_bf16(const uint16_t* x, int64_t rows, int64_t k, bool rotate, uint8_t* codes,
                                 uint8_t* scales, hipStream_t stream);
-hipError_t launch_mx_quant_f32(const float* x, int64_t rows, int64_t k, uint8_t* codes, uint8_t* scales,
-                               hipStream_t stream);
+hipError_t launch_mx_quant_f32(const float* x, int64_t rows, int64_t k, bool rotate, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream);
 // out [m, n] bf16 = A [m, k] . B [n, k]^T over the decoded MXFP4 values.
 hipError_t launch_gemm_mx(const uint8_t* a_codes, const uint8_t* a_scales, const uint8_t* b_codes,
                           const uint8_t* b_scales, int64_t m, int64_t n, int64_t k, uint16_t* out,

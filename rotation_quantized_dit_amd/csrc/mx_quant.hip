@@ -14,9 +14,17 @@
 // Rounding needs no table: the magnitude code counts the midpoints that |y|
 // passes, with >= where the tie goes up to the even code (0.75, 1.75, 3.5)
 // and > where it stays at the even code below (0.25, 1.25, 2.5, 5).
+//
+// Rotated variant: the rows are first rotated along K with the orthonormal
+// Hadamard of size 256, group by group, exactly as the int8 ConvRot
+// quantizer rotates them (the same butterfly, stage order and 1/16), and the
+// rotated values are then quantized as above.  Rotating both operands keeps
+// their product unchanged, and spreads the outlier channels that would
+// otherwise set the scale of their whole 32-element block.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fwht.h"
 #include "kernels.h"
 
 namespace convrot {
@@ -86,6 +94,72 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(Src src, int64_t rows, in
     }
 }
 
+// Rotated variant: one 256-group per 16 lanes (4 per wave, 16 per
+// workgroup).  Lane j loads elements 16 j .. 16 j + 15, the butterfly runs as
+// in the rotate pass, and the normalized results go back through the lane's
+// tile to natural order; lanes 2p and 2p + 1 then hold one 32-element block.
+template <typename Src>
+__global__ __launch_bounds__(256) void rot_mx_quant_kernel(Src src, int64_t rows, int64_t k,
+                                                           uint8_t* __restrict__ codes,
+                                                           uint8_t* __restrict__ scales) {
+    __shared__ float tiles[16 * kTile];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int sub = lane >> 4;
+    const int j = lane & 15;
+    const int64_t G = k >> 8;
+    const int64_t gid = (int64_t)blockIdx.x * 16 + wave * 4 + sub;
+    const bool ok = gid < rows * G;
+    const int64_t row = ok ? gid / G : 0;
+    const int64_t col = (ok ? gid % G : 0) * 256 + j * 16;
+    float* tile = tiles + (wave * 4 + sub) * kTile;
+
+    float v[16];
+    if (ok) {
+        src.load8(row * k + col, v);
+        src.load8(row * k + col + 8, v + 8);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 16; ++i) v[i] = 0.0f;
+    }
+    butterfly16(v);
+    transpose_phase2(tile, j, v);          // lane j: rotated elements j + 16 b (unnormalized)
+#pragma unroll
+    for (int b = 0; b < 16; ++b) tile[b * 17 + j] = v[b] * 0.0625f;
+    wave_fence();
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = tile[j * 17 + i];   // elements 16 j .. 16 j + 15
+    wave_fence();
+    float amax = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[e]));
+    amax = __builtin_fmaxf(amax, __shfl_xor(amax, 1, 64));
+    const int ef = (int)((__float_as_uint(amax) >> 23) & 0xff);
+    const int scode = ef >= 2 ? ef - 2 : 0;
+    const float inv_scale = __uint_as_float((uint32_t)(254 - scode) << 23);
+    uint32_t lo = 0, hi = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        lo |= e2m1_code(v[e], inv_scale) << (4 * e);
+        hi |= e2m1_code(v[8 + e], inv_scale) << (4 * e);
+    }
+    if (ok) {
+        *reinterpret_cast<uint2*>(codes + row * (k / 2) + col / 2) = make_uint2(lo, hi);
+        if ((j & 1) == 0) scales[row * (k / 32) + col / 32] = (uint8_t)scode;
+    }
+}
+
+template <typename Src>
+hipError_t launch_rot(Src src, int64_t rows, int64_t k, uint8_t* codes, uint8_t* scales,
+                      hipStream_t stream) {
+    const int64_t groups = rows * (k / 256);
+    const unsigned grid = (unsigned)((groups + 15) / 16);
+    hipLaunchKernelGGL(rot_mx_quant_kernel<Src>, dim3(grid), dim3(256), 0, stream, src, rows, k, codes,
+                       scales);
+    return hipGetLastError();
+}
+
 template <typename Src>
 hipError_t launch(Src src, int64_t rows, int64_t k, uint8_t* codes, uint8_t* scales, hipStream_t stream) {
     const int64_t threads = rows * (k / 8);
@@ -96,14 +170,16 @@ hipError_t launch(Src src, int64_t rows, int64_t k, uint8_t* codes, uint8_t* sca
 
 }  // namespace
 
-hipError_t launch_mx_quant_bf16(const uint16_t* x, int64_t rows, int64_t k, uint8_t* codes,
+hipError_t launch_mx_quant_bf16(const uint16_t* x, int64_t rows, int64_t k, bool rotate, uint8_t* codes,
                                 uint8_t* scales, hipStream_t stream) {
-    return launch(Bf16Src{x}, rows, k, codes, scales, stream);
+    return rotate ? launch_rot(Bf16Src{x}, rows, k, codes, scales, stream)
+                  : launch(Bf16Src{x}, rows, k, codes, scales, stream);
 }
 
-hipError_t launch_mx_quant_f32(const float* x, int64_t rows, int64_t k, uint8_t* codes, uint8_t* scales,
-                               hipStream_t stream) {
-    return launch(F32Src{x}, rows, k, codes, scales, stream);
+hipError_t launch_mx_quant_f32(const float* x, int64_t rows, int64_t k, bool rotate, uint8_t* codes,
+                               uint8_t* scales, hipStream_t stream) {
+    return rotate ? launch_rot(F32Src{x}, rows, k, codes, scales, stream)
+                  : launch(F32Src{x}, rows, k, codes, scales, stream);
 }
 
 }  // namespace convrot

@@ -220,3 +220,29 @@ def test_attention_validation(L):
     assert L.convrot_attention(None, None, None, 768, 0, 2, 128, None, 256, None, 0, None) == OK
     assert L.convrot_attention_prep(None, None, None, 0, 10, 0, 128, None, 0, None) == OK
     assert L.convrot_attention_prepared(None, 0, 0, 3, 128, None, 384, None) == OK
+
+
+def test_mx_validation(L):
+    """MXFP4 entry points: k multiple of 128 (256 when rotating), pointers,
+    workspace; empty calls are no-ops."""
+    from rotation_quantized_dit_amd._lib import ERR_ALIGN, ERR_NULL, ERR_SHAPE, ERR_WORKSPACE, OK
+    assert L.convrot_mx_quantize_act(A, 4, 200, 0, B, C, None) == ERR_SHAPE
+    assert L.convrot_mx_quantize_act(A, 4, 384, 1, B, C, None) == ERR_SHAPE
+    assert L.convrot_mx_quantize_act(A, -1, 256, 0, B, C, None) == ERR_SHAPE
+    assert L.convrot_mx_quantize_act(None, 4, 256, 0, B, C, None) == ERR_NULL
+    assert L.convrot_mx_quantize_act(MIS, 4, 256, 0, B, C, None) == ERR_ALIGN
+    assert L.convrot_mx_quantize_act(None, 0, 256, 1, None, None, None) == OK
+    assert L.convrot_mx_quantize_weight(A, 4, (1 << 20) + 128, 0, B, C, None) == ERR_SHAPE
+    assert L.convrot_mx_quantize_weight(A, 4, 256, 0, None, C, None) == ERR_NULL
+    assert L.convrot_mx_gemm(A, B, C, D, 4, 4, 100, A, None) == ERR_SHAPE
+    assert L.convrot_mx_gemm(A, B, C, None, 4, 4, 128, A, None) == ERR_NULL
+    assert L.convrot_mx_gemm(A, B, C, D, 4, 4, 128, MIS, None) == ERR_ALIGN
+    assert L.convrot_mx_gemm(None, None, None, None, 0, 4, 128, None, None) == OK
+    need = L.convrot_mx_workspace_bytes(10, 512)
+    assert need == 2560 + 10 * 16
+    assert L.convrot_mx_workspace_bytes(10, 100) == 0
+    assert L.convrot_mx_linear(A, 10, 512, 0, B, C, 4, D, D, need - 1, None) == ERR_WORKSPACE
+    assert L.convrot_mx_linear(A, 10, 512, 0, B, C, 4, D, None, need, None) == ERR_WORKSPACE
+    assert L.convrot_mx_linear(A, 10, 512, 0, B, C, 4, D, MIS, need, None) == ERR_ALIGN
+    assert L.convrot_mx_linear(A, 10, 384, 1, B, C, 4, D, D, need, None) == ERR_SHAPE
+    assert L.convrot_mx_linear(None, 0, 512, 0, None, None, 4, None, None, 0, None) == OK

@@ -57,27 +57,35 @@ def edge_rows(k, rng):
     return np.stack(rows)
 
 
-@pytest.mark.parametrize("m,k", [(1, 128), (7, 256), (64, 512), (300, 5376), (33, 14336)])
-def test_mx_quantize_parity(cr, m, k):
+@pytest.mark.parametrize("m,k,rotate", [(1, 128, False), (7, 256, False), (64, 512, False),
+                                        (300, 5376, False), (33, 14336, False), (1, 256, True),
+                                        (9, 512, True), (300, 5376, True), (33, 14336, True)])
+def test_mx_quantize_parity(cr, m, k, rotate):
     import torch
     rng = np.random.default_rng(200 + m)
     x = rng.standard_normal((m, k)).astype(np.float32) * rng.choice([0.01, 1, 30], size=(m, 1)).astype(np.float32)
     x = np.concatenate([x, edge_rows(k, rng)])
     xb = workloads.to_bf16_bits(x)
-    qc_d, qs_d = cr.mx_quantize_act(gu.dev_bf16(xb))
-    wc_d, ws_d = cr.mx_quantize_weight(gu.dev(x))
+    qc_d, qs_d = cr.mx_quantize_act(gu.dev_bf16(xb), rotate=rotate)
+    wc_d, ws_d = cr.mx_quantize_weight(gu.dev(x), rotate=rotate)
     torch.cuda.synchronize()
-    qc, qs = oracle.mx_quantize_act(xb)
-    wc, ws = oracle.mx_quantize(x)
+    if rotate:
+        qc, qs = oracle.mx_quantize_act_rotated(xb)
+        wc, ws = oracle.mx_quantize_rotated(x)
+    else:
+        qc, qs = oracle.mx_quantize_act(xb)
+        wc, ws = oracle.mx_quantize(x)
     gu.assert_equal(gu.host(qc_d), qc, "activation codes")
     gu.assert_equal(gu.host(qs_d), qs, "activation scales")
     gu.assert_equal(gu.host(wc_d), wc, "weight codes")
     gu.assert_equal(gu.host(ws_d), ws, "weight scales")
 
 
-@pytest.mark.parametrize("m,n,k", [(1, 1, 128), (5, 37, 128), (64, 256, 256), (257, 300, 384),
-                                   (300, 513, 5376), (512, 64, 14336)])
-def test_mx_gemm_parity(cr, m, n, k):
+@pytest.mark.parametrize("m,n,k,rotate", [(1, 1, 128, False), (5, 37, 128, False), (64, 256, 256, False),
+                                          (257, 300, 384, False), (300, 513, 5376, False),
+                                          (512, 64, 14336, False), (33, 70, 256, True),
+                                          (300, 513, 5376, True)])
+def test_mx_gemm_parity(cr, m, n, k, rotate):
     import torch
     rng = np.random.default_rng(300 + m + n)
     x = rng.standard_normal((m, k)).astype(np.float32)
@@ -85,13 +93,17 @@ def test_mx_gemm_parity(cr, m, n, k):
     w = (rng.standard_normal((n, k)) * 0.02).astype(np.float32)
     xb = workloads.to_bf16_bits(x)
     xd, wd = gu.dev_bf16(xb), gu.dev(w)
-    ac, asc = cr.mx_quantize_act(xd)
-    bc, bsc = cr.mx_quantize_weight(wd)
+    ac, asc = cr.mx_quantize_act(xd, rotate=rotate)
+    bc, bsc = cr.mx_quantize_weight(wd, rotate=rotate)
     y = cr.mx_gemm(ac, asc, bc, bsc)
-    y2 = cr.mx_linear(xd, bc, bsc)
+    y2 = cr.mx_linear(xd, bc, bsc, rotate=rotate)
     torch.cuda.synchronize()
-    oac, oas = oracle.mx_quantize_act(xb)
-    obc, obs = oracle.mx_quantize(w)
+    if rotate:
+        oac, oas = oracle.mx_quantize_act_rotated(xb)
+        obc, obs = oracle.mx_quantize_rotated(w)
+    else:
+        oac, oas = oracle.mx_quantize_act(xb)
+        obc, obs = oracle.mx_quantize(w)
     gu.assert_equal(gu.host(ac), oac, "A codes")
     gu.assert_equal(gu.host(bc), obc, "B codes")
     ref, absacc = oracle.mx_gemm(oac, oas, obc, obs)
@@ -128,10 +140,13 @@ def test_mx_validation(cr):
     x = torch.zeros(4, 200, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(cr.ConvRotError):
         cr.mx_quantize_act(x)                       # k not a multiple of 128
+    x2 = torch.zeros(4, 384, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(cr.ConvRotError):
+        cr.mx_quantize_act(x2, rotate=True)         # rotation needs whole 256-groups
 
 
-@pytest.mark.parametrize("name", ["qkv", "ffn_up"])
-def test_mx_full_size(cr, name):
+@pytest.mark.parametrize("name,rotate", [("qkv", False), ("ffn_up", False), ("qkv", True)])
+def test_mx_full_size(cr, name, rotate):
     """The QKV (4096 x 5376 -> 16128) and FFN-input (32256 x 5376 -> 28672)
     shapes: every activation and weight code and scale bit for bit, and the
     product on sampled rows (first, last, 64 seeded)."""
@@ -140,17 +155,21 @@ def test_mx_full_size(cr, name):
     print("mx full size %s: generating" % name, flush=True)
     d = workloads.make_linear(name)
     xd, wd = gu.dev_bf16(d["x"]), gu.dev(d["w"])
-    ac, asc = cr.mx_quantize_act(xd)
-    bc, bsc = cr.mx_quantize_weight(wd)
-    y = cr.mx_linear(xd, bc, bsc)
+    ac, asc = cr.mx_quantize_act(xd, rotate=rotate)
+    bc, bsc = cr.mx_quantize_weight(wd, rotate=rotate)
+    y = cr.mx_linear(xd, bc, bsc, rotate=rotate)
     torch.cuda.synchronize()
     rows = workloads.sample_rows(c.m, seed=c.seed)
     g = dict(ac=gu.host(ac), asc=gu.host(asc), bc=gu.host(bc), bsc=gu.host(bsc),
              y=gu.host_bf16(y[torch.from_numpy(rows).cuda()]))
     del xd, wd, ac, asc, bc, bsc, y
     print("mx full size %s: oracle" % name, flush=True)
-    oac, oas = oracle.mx_quantize_act(d["x"])
-    obc, obs = oracle.mx_quantize(d["w"])
+    if rotate:
+        oac, oas = oracle.mx_quantize_act_rotated(d["x"])
+        obc, obs = oracle.mx_quantize_rotated(d["w"])
+    else:
+        oac, oas = oracle.mx_quantize_act(d["x"])
+        obc, obs = oracle.mx_quantize(d["w"])
     gu.assert_equal(g["ac"], oac, name + " activation codes")
     gu.assert_equal(g["asc"], oas, name + " activation scales")
     gu.assert_equal(g["bc"], obc, name + " weight codes")

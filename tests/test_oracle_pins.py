@@ -942,3 +942,30 @@ def test_mx_gemm_against_dense():
     assert np.array_equal(y, ref)
     assert np.all(np.abs(y) <= absacc)
     assert np.allclose(absacc, np.abs(oracle.mx_decode(ac, asc)) @ np.abs(oracle.mx_decode(bc, bsc)).T)
+
+
+def test_mx_rotated_composition():
+    """Rotated MXFP4: rotating the decoded values back (H/16 is its own
+    inverse) returns the input within the block error in the rotated basis
+    (the rotation preserves every 256-group's norm), and the product of two
+    rotated operands approximates the unrotated product x W^T; on rows with
+    an outlier channel the rotated format is closer to x W^T than the plain
+    one (the reason to rotate)."""
+    rng = np.random.default_rng(73)
+    x = rng.standard_normal((24, 512)).astype(np.float32)
+    x[:, 7] *= 30
+    w = (rng.standard_normal((16, 512)) * 0.02).astype(np.float32)
+    xc, xs = oracle.mx_quantize_rotated(x)
+    d = oracle.mx_decode(xc, xs)
+    back = oracle.rotate_rows(d.astype(np.float32)).astype(np.float64)
+    r = oracle.rotate_rows(x).astype(np.float64)
+    for g in range(2):
+        sl = slice(256 * g, 256 * g + 256)
+        assert np.allclose(np.linalg.norm(back[:, sl] - x[:, sl], axis=1),
+                           np.linalg.norm(d[:, sl] - r[:, sl], axis=1), rtol=1e-5, atol=1e-6)
+    y_rot, _ = oracle.mx_gemm(xc, xs, *oracle.mx_quantize_rotated(w))
+    y_plain, _ = oracle.mx_gemm(*oracle.mx_quantize(x), *oracle.mx_quantize(w))
+    ref = x.astype(np.float64) @ w.astype(np.float64).T
+    e_rot = np.linalg.norm(y_rot - ref) / np.linalg.norm(ref)
+    e_plain = np.linalg.norm(y_plain - ref) / np.linalg.norm(ref)
+    assert e_rot < 0.2 and e_rot < e_plain, (e_rot, e_plain)
