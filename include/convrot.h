@@ -276,7 +276,11 @@ int convrot_attention(const uint16_t* q, const uint16_t* k, const uint16_t* v, i
  *              product of two rotated operands and spreads outlier channels
  *              across their group; rotate == 0 is the plain format, like the
  *              hybrid's 4-bit layers, which carry no rotation.
- * Layouts: codes [rows, k/2] bytes, scales [rows, k/32] bytes, row-major.
+ * Layouts: codes [rows, k/2] bytes, row-major; scales chunk-major
+ * [k/128][rows][4] bytes -- the scale of block b of row r is byte
+ * (b / 4) * rows * 4 + r * 4 + b % 4 -- so that the four scales of one
+ * 128-element chunk of consecutive rows are contiguous, as the product
+ * streams them.
  * k must be a positive multiple of 128 (256 when rotating), at most 2^20.
  * Pointers 16-byte aligned; sizes checked first; rows == 0 is a no-op.
  * Both operands of a product must be quantized with the same rotate flag.
@@ -302,7 +306,7 @@ size_t convrot_mx_workspace_bytes(int64_t m, int64_t k);
 
 /* MXFP4 linear: quantize x [m, k] (bf16; rotated if rotate) into the
  * workspace, then the product with a weight prepared with the same rotate
- * flag (codes [n, k/2], scales [n, k/32]).                                  */
+ * flag (codes [n, k/2], scales [k/128][n][4]).                              */
 int convrot_mx_linear(const uint16_t* x, int64_t m, int64_t k, int rotate, const uint8_t* w_codes,
                       const uint8_t* w_scales, int64_t n, uint16_t* out, void* workspace,
                       size_t workspace_bytes, void* stream);

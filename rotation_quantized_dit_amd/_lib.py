@@ -401,13 +401,14 @@ def attention(q, k, v, heads: int, out=None, workspace=None):
 
 def _mx_outputs(rows, k, like, codes, scales):
     codes = _out(codes, (rows, k // 2), torch.uint8, like, "codes")
-    scales = _out(scales, (rows, k // 32), torch.uint8, like, "scales")
+    scales = _out(scales, (k // 128, rows, 4), torch.uint8, like, "scales")
     return codes, scales
 
 
 def mx_quantize_act(x: torch.Tensor, codes=None, scales=None, rotate=False):
-    """bf16 x [m, k] -> MXFP4 (codes [m, k/2] uint8, E8M0 scales [m, k/32] uint8),
-    of the Hadamard-256-rotated rows if ``rotate``."""
+    """bf16 x [m, k] -> MXFP4: codes [m, k/2] uint8 and E8M0 scales
+    [k/128, m, 4] uint8 (chunk-major), of the Hadamard-256-rotated rows if
+    ``rotate``."""
     _dev(x, "x", torch.bfloat16, 2)
     m, k = x.shape
     codes, scales = _mx_outputs(m, k, x, codes, scales)
@@ -428,13 +429,15 @@ def mx_quantize_weight(w: torch.Tensor, codes=None, scales=None, rotate=False):
 
 def mx_gemm(a_codes, a_scales, b_codes, b_scales, out=None):
     """bf16 [m, n] = A . B^T of MXFP4 operands."""
-    for t, nm in ((a_codes, "a_codes"), (a_scales, "a_scales"), (b_codes, "b_codes"), (b_scales, "b_scales")):
-        _dev(t, nm, torch.uint8, 2)
+    _dev(a_codes, "a_codes", torch.uint8, 2)
+    _dev(b_codes, "b_codes", torch.uint8, 2)
+    _dev(a_scales, "a_scales", torch.uint8, 3)
+    _dev(b_scales, "b_scales", torch.uint8, 3)
     m, k2 = a_codes.shape
     n = b_codes.shape[0]
     k = 2 * k2
-    if (b_codes.shape[1] != k2 or tuple(a_scales.shape) != (m, k // 32)
-            or tuple(b_scales.shape) != (n, k // 32)):
+    if (b_codes.shape[1] != k2 or tuple(a_scales.shape) != (k // 128, m, 4)
+            or tuple(b_scales.shape) != (k // 128, n, 4)):
         raise ValueError("MXFP4 operand shapes do not match")
     y = _out(out, (m, n), torch.bfloat16, a_codes, "out")
     _check("convrot_mx_gemm", load_library().convrot_mx_gemm(
@@ -453,10 +456,10 @@ def mx_linear(x: torch.Tensor, w_codes: torch.Tensor, w_scales: torch.Tensor, ou
     with the same ``rotate`` flag."""
     _dev(x, "x", torch.bfloat16, 2)
     _dev(w_codes, "w_codes", torch.uint8, 2)
-    _dev(w_scales, "w_scales", torch.uint8, 2)
+    _dev(w_scales, "w_scales", torch.uint8, 3)
     m, k = x.shape
     n = w_codes.shape[0]
-    if w_codes.shape[1] != k // 2 or tuple(w_scales.shape) != (n, k // 32):
+    if w_codes.shape[1] != k // 2 or tuple(w_scales.shape) != (k // 128, n, 4):
         raise ValueError("weight shapes do not match x %s" % (tuple(x.shape),))
     y = _out(out, (m, n), torch.bfloat16, x, "out")
     need = max(mx_workspace_bytes(m, k), 16)

@@ -8,7 +8,8 @@
 //   the MFMA and accumulates in fp32.
 //
 // Operands: codes [rows, K/2] bytes (element 2j in the low nibble of byte j)
-// and E8M0 scales [rows, K/32] bytes.  In bytes, a 64-element k-step of FP4
+// and E8M0 scales chunk-major, [K/128][rows][4] bytes (the 4 block scales of
+// one 128-element chunk of consecutive rows are contiguous).  In bytes, a 64-element k-step of FP4
 // occupies 32 bytes of a row and each lane takes 16 of them (lanes 0-31 the
 // first 32 elements, lanes 32-63 the next 32), exactly the layout of the
 // int8 operands of K-GEMM; so the tiling below is that kernel's 256-row
@@ -17,9 +18,11 @@
 // 4-slot LDS ring of direct buffer loads, XOR-swizzled 64-byte rows.
 // Each stage also carries one 32-bit word per tile row: the 4 block scales
 // of that row's 128 elements, copied by 4-byte direct loads (one per wave:
-// waves 0-3 the 256 A rows, waves 4-7 the 256 B rows).  A lane shifts each
-// word right by 8 x (lane / 32), so byte 0 is the scale of its block in the
-// first k-step and byte 2 in the second (the MFMA's scale byte select).
+// waves 0-3 the 256 A rows, waves 4-7 the 256 B rows), 256 contiguous bytes
+// per copy in the chunk-major layout (row-major scales would put each lane's
+// word in a different cache line, which measured 30 % slower).  For k-step s a lane
+// reads the one byte it needs, block 2 s + lane / 32 of its row, with a byte
+// load from LDS, so the scale operand needs no vector instruction.
 //
 // Ragged rows are clamped to the last row for loading and masked at the
 // store; K must be a multiple of 128.
@@ -129,13 +132,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
     const int rows_a = (M - m0) < BM ? (M - m0) : BM;
     const int rows_b = (N - n0) < BN ? (N - n0) : BN;
     const int KB = K / 2;                    // code bytes per row
-    const int KS = K / 32;                   // scale bytes per row
 
     const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(A + (int64_t)m0 * KB, (uint32_t)rows_a * (uint32_t)KB);
     const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(B + (int64_t)n0 * KB, (uint32_t)rows_b * (uint32_t)KB);
+    // scales of this tile's rows: chunk kt at byte kt * rows_total * 4 from
+    // the tile's first row (the resource spans every chunk of those rows)
+    const int KT_ = K / 128;
     const __amdgpu_buffer_rsrc_t rsrc_s =
-        wave < 4 ? make_rsrc(SA + (int64_t)m0 * KS, (uint32_t)rows_a * (uint32_t)KS)
-                 : make_rsrc(SB + (int64_t)n0 * KS, (uint32_t)rows_b * (uint32_t)KS);
+        wave < 4 ? make_rsrc(SA + (int64_t)m0 * 4, (uint32_t)((int64_t)(KT_ - 1) * M * 4 + rows_a * 4))
+                 : make_rsrc(SB + (int64_t)n0 * 4, (uint32_t)((int64_t)(KT_ - 1) * N * 4 + rows_b * 4));
+    const uint32_t chunk_stride = (uint32_t)(wave < 4 ? M : N) * 4u;
 
     // Copy sources: copy i < MA of wave w fills A rows 16 (MA w + i) .. +15,
     // copies MA, MA + 1 fill B rows 32 w + 16 (i - MA) .. +15 (lane l: row
@@ -152,7 +158,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
     }
     const int srow = 64 * (wave & 3) + lane;
     const int slim = wave < 4 ? rows_a : rows_b;
-    const uint32_t voff_s = (uint32_t)(srow < slim ? srow : slim - 1) * (uint32_t)KS;
+    const uint32_t voff_s = (uint32_t)(srow < slim ? srow : slim - 1) * 4u;
     auto issue = [&](int kt, int slot) {
         uint8_t* st = lds + slot * STAGE_BYTES;
         const uint32_t soff = (uint32_t)kt * BK;
@@ -160,7 +166,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
         for (int i = 0; i < MA; ++i) copy16(rsrc_a, st + 16 * 64 * MA * wave + 1024 * i, voff[i], soff);
         copy16(rsrc_b, st + A_STAGE + 32 * 64 * wave, voff[MA], soff);
         copy16(rsrc_b, st + A_STAGE + 32 * 64 * wave + 1024, voff[MA + 1], soff);
-        copy4(rsrc_s, st + A_STAGE + B_STAGE + 256 * wave, voff_s, (uint32_t)kt * 4u);
+        copy4(rsrc_s, st + A_STAGE + B_STAGE + 256 * wave, voff_s, (uint32_t)kt * chunk_stride);
     };
 
     int a_row[MA], b_row[4];
@@ -186,40 +192,40 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
 #pragma unroll
         for (int b = 0; b < 4; ++b) b_off[s][b] = A_STAGE + b_row[b] * BK + 16 * (c ^ swz(b_row[b]));
     }
-    // Scale words of this lane's rows for a stage, shifted so that byte 0 is
-    // its block of k-step 0 and byte 2 its block of k-step 1.
-    auto read_scales = [&](const uint8_t* st, int (&sa)[MA], int (&sb)[4]) {
+    // Byte offsets (within a stage) of this lane's scale bytes for k-step s:
+    // block 2 s + g of the lane's A rows and B rows.
+    int sa_off[2][MA], sb_off[2][4];
 #pragma unroll
-        for (int a = 0; a < MA; ++a)
-            sa[a] = (int)(*reinterpret_cast<const uint32_t*>(st + A_STAGE + B_STAGE + 4 * (32 * MA * wm + 32 * a + (lane & 31))) >> (8 * g));
+    for (int s = 0; s < 2; ++s) {
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-            sb[b] = (int)(*reinterpret_cast<const uint32_t*>(st + A_STAGE + B_STAGE + 4 * BM + 4 * b_row[b]) >> (8 * g));
-    };
-    auto read_frags = [&](const uint8_t* st, int s, v4i (&af)[MA], v4i (&bf)[4]) {
+        for (int a = 0; a < MA; ++a) sa_off[s][a] = A_STAGE + B_STAGE + 4 * a_row[a] + 2 * s + g;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) sb_off[s][b] = A_STAGE + B_STAGE + 4 * BM + 4 * b_row[b] + 2 * s + g;
+    }
+    // Fragments and scale bytes of k-step s of a stage.
+    auto read_frags = [&](const uint8_t* st, int s, v4i (&af)[MA], v4i (&bf)[4], int (&sa)[MA], int (&sb)[4]) {
 #pragma unroll
         for (int a = 0; a < MA; ++a) af[a] = *reinterpret_cast<const v4i*>(st + a_off[s][a]);
 #pragma unroll
         for (int b = 0; b < 4; ++b) bf[b] = *reinterpret_cast<const v4i*>(st + b_off[s][b]);
+#pragma unroll
+        for (int a = 0; a < MA; ++a) sa[a] = st[sa_off[s][a]];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) sb[b] = st[sb_off[s][b]];
     };
-    auto mma = [&](int s, const v4i (&af)[MA], const v4i (&bf)[4], const int (&sa)[MA], const int (&sb)[4]) {
+    auto mma = [&](const v4i (&af)[MA], const v4i (&bf)[4], const int (&sa)[MA], const int (&sb)[4]) {
 #pragma unroll
         for (int a = 0; a < MA; ++a)
 #pragma unroll
             for (int b = 0; b < 4; ++b) {
                 const v8i av = {af[a].x, af[a].y, af[a].z, af[a].w, 0, 0, 0, 0};
                 const v8i bv = {bf[b].x, bf[b].y, bf[b].z, bf[b].w, 0, 0, 0, 0};
-                if (s == 0)
-                    acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[a][b], 4, 4, 0,
-                                                                                sa[a], 0, sb[b]);
-                else
-                    acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[a][b], 4, 4, 2,
-                                                                                sa[a], 2, sb[b]);
+                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[a][b], 4, 4, 0, sa[a], 0,
+                                                                            sb[b]);
             }
     };
 
-    constexpr int NREAD = MA + 4;
-    constexpr int NMFMA = 4 * MA;
+    static_assert(MA == 2 && COPIES == 5, "the interleave patterns below count 8 MFMAs, 12 reads, 5 copies");
     const int KT = K / 128;
     // conditional prologue and branchy wait, as in K-GEMM (an unconditional
     // one makes the compiler drain the ring before every stage's first read)
@@ -235,55 +241,72 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
     }
     lds_barrier();
 
+    // Software pipeline (as K-GEMM's 256-row variant): in stage kt, k-step 0
+    // runs on register set 0 while k-step 1's operands are read into set 1;
+    // after the barrier, k-step 1 runs on set 1 while the slot is refilled
+    // with stage kt + STAGES and stage kt + 1's k-step 0 is read into set 0.
     int kt = 0;
     int slot = 0;
     v4i fa0[MA], fb0[4], fa1[MA], fb1[4];
-    int sa[MA], sb[4];
-    read_scales(lds, sa, sb);
-    read_frags(lds, 0, fa0, fb0);
+    int sa0[MA], sb0[4], sa1[MA], sb1[4];
+    read_frags(lds, 0, fa0, fb0, sa0, sb0);
     for (; kt + STAGES < KT; ++kt) {
         const int next = slot + 1 == STAGES ? 0 : slot + 1;
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1);
-        mma(0, fa0, fb0, sa, sb);
+        read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1, sa1, sb1);
+        mma(fa0, fb0, sa0, sb0);
+        // 8 MFMAs, 12 LDS reads (6 fragments, 6 scale bytes)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+        }
+#pragma unroll
+        for (int i = 4; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
-        int sa_n[MA], sb_n[4];
         wait_vmcnt<(STAGES - 2) * COPIES>();
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(lds + next * STAGE_BYTES, 0, fa0, fb0);
-        read_scales(lds + next * STAGE_BYTES, sa_n, sb_n);
+        read_frags(lds + next * STAGE_BYTES, 0, fa0, fb0, sa0, sb0);
         issue(kt + STAGES, slot);
-        mma(1, fa1, fb1, sa, sb);
+        mma(fa1, fb1, sa1, sb1);
+        // 8 MFMAs, 12 LDS reads and the 5 copies of the refill
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
+            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one direct copy
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+#pragma unroll
+        for (int i = 5; i < 8; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        }
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int a = 0; a < MA; ++a) sa[a] = sa_n[a];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) sb[b] = sb_n[b];
         slot = next;
     }
     for (; kt + 1 < KT; ++kt) {
         const int next = slot + 1 == STAGES ? 0 : slot + 1;
-        read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1);
-        mma(0, fa0, fb0, sa, sb);
+        read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1, sa1, sb1);
+        mma(fa0, fb0, sa0, sb0);
         const int after = KT - 2 - kt;
         if (after >= 2) wait_vmcnt<2 * COPIES>();
         else if (after >= 1) wait_vmcnt<COPIES>();
         else wait_vmcnt<0>();
         lds_barrier();
-        int sa_n[MA], sb_n[4];
-        read_frags(lds + next * STAGE_BYTES, 0, fa0, fb0);
-        read_scales(lds + next * STAGE_BYTES, sa_n, sb_n);
-        mma(1, fa1, fb1, sa, sb);
-#pragma unroll
-        for (int a = 0; a < MA; ++a) sa[a] = sa_n[a];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) sb[b] = sb_n[b];
+        read_frags(lds + next * STAGE_BYTES, 0, fa0, fb0, sa0, sb0);
+        mma(fa1, fb1, sa1, sb1);
         slot = next;
     }
-    read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1);
-    mma(0, fa0, fb0, sa, sb);
-    mma(1, fa1, fb1, sa, sb);
+    read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1, sa1, sb1);
+    mma(fa0, fb0, sa0, sb0);
+    mma(fa1, fb1, sa1, sb1);
 
     // Epilogue: each wave parks a 32 x 128 block of fp32 accumulators in its
     // part of the freed ring and writes it back as bf16, 8 consecutive columns

@@ -48,7 +48,7 @@ hipError_t launch_attn_flash(const int8_t* qc, const float* sq, const int8_t* kc
 // MXFP4: block-32 E8M0 scales + FP4 E2M1 codes (two per byte) of rows of k
 // elements (k % 128 == 0; with rotate, k % 256 == 0 and the rows are first
 // rotated by the Hadamard-256 of the int8 path): codes [rows, k/2], scales
-// [rows, k/32].
+// chunk-major [k/128][rows][4].
 hipError_t launch_mx_quant_bf16(const uint16_t* x, int64_t rows, int64_t k, bool rotate, uint8_t* codes,
                                 uint8_t* scales, hipStream_t stream);
 hipError_t launch_mx_quant_f32(const float* x, int64_t rows, int64_t k, bool rotate, uint8_t* codes,

@@ -11,6 +11,10 @@
 //            nearest of 0, 0.5, 1, 1.5, 2, 3, 4, 6 (ties to the even
 //            mantissa bit, saturating at 6);
 //   packed: element 2j in the low nibble of byte j.
+// Scales are stored chunk-major, as the GEMM streams them: the scale of block
+// b of row r (of `rows`) is byte (b / 4) * rows * 4 + r * 4 + b % 4, i.e. a
+// [k/128][rows][4] array, so that the four scales of one 128-element chunk of
+// consecutive rows are contiguous.
 // Rounding needs no table: the magnitude code counts the midpoints that |y|
 // passes, with >= where the tie goes up to the even code (0.75, 1.75, 3.5)
 // and > where it stays at the even code below (0.25, 1.25, 2.5, 5).
@@ -90,7 +94,10 @@ __global__ __launch_bounds__(256) void mx_quant_kernel(Src src, int64_t rows, in
     for (int e = 0; e < 8; ++e) packed |= e2m1_code(v[e], inv_scale) << (4 * e);
     if (live) {
         *reinterpret_cast<uint32_t*>(codes + row * (k / 2) + col / 2) = packed;
-        if ((col & 31) == 0) scales[row * (k / 32) + col / 32] = (uint8_t)scode;
+        if ((col & 31) == 0) {
+            const int64_t b = col / 32;
+            scales[(b >> 2) * rows * 4 + row * 4 + (b & 3)] = (uint8_t)scode;
+        }
     }
 }
 
@@ -146,7 +153,10 @@ __global__ __launch_bounds__(256) void rot_mx_quant_kernel(Src src, int64_t rows
     }
     if (ok) {
         *reinterpret_cast<uint2*>(codes + row * (k / 2) + col / 2) = make_uint2(lo, hi);
-        if ((j & 1) == 0) scales[row * (k / 32) + col / 32] = (uint8_t)scode;
+        if ((j & 1) == 0) {
+            const int64_t b = col / 32;
+            scales[(b >> 2) * rows * 4 + row * 4 + (b & 3)] = (uint8_t)scode;
+        }
     }
 }
 

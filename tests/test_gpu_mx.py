@@ -21,6 +21,13 @@ def cr():
     return cr
 
 
+def natural_scales(chunked):
+    """Chunk-major [k/128, rows, 4] scales (the library's layout) -> the
+    natural [rows, k/32] (a relayout, no arithmetic)."""
+    c = np.asarray(chunked)
+    return np.ascontiguousarray(c.transpose(1, 0, 2).reshape(c.shape[1], -1))
+
+
 def assert_mx_product(y_bits, ref, absacc, k, what):
     g = gu.bf16_f64(y_bits)
     err = np.abs(g - ref)
@@ -76,9 +83,9 @@ def test_mx_quantize_parity(cr, m, k, rotate):
         qc, qs = oracle.mx_quantize_act(xb)
         wc, ws = oracle.mx_quantize(x)
     gu.assert_equal(gu.host(qc_d), qc, "activation codes")
-    gu.assert_equal(gu.host(qs_d), qs, "activation scales")
+    gu.assert_equal(natural_scales(gu.host(qs_d)), qs, "activation scales")
     gu.assert_equal(gu.host(wc_d), wc, "weight codes")
-    gu.assert_equal(gu.host(ws_d), ws, "weight scales")
+    gu.assert_equal(natural_scales(gu.host(ws_d)), ws, "weight scales")
 
 
 @pytest.mark.parametrize("m,n,k,rotate", [(1, 1, 128, False), (5, 37, 128, False), (64, 256, 256, False),
@@ -106,6 +113,8 @@ def test_mx_gemm_parity(cr, m, n, k, rotate):
         obc, obs = oracle.mx_quantize(w)
     gu.assert_equal(gu.host(ac), oac, "A codes")
     gu.assert_equal(gu.host(bc), obc, "B codes")
+    gu.assert_equal(natural_scales(gu.host(asc)), oas, "A scales")
+    gu.assert_equal(natural_scales(gu.host(bsc)), obs, "B scales")
     ref, absacc = oracle.mx_gemm(oac, oas, obc, obs)
     yb = gu.host_bf16(y)
     assert_mx_product(yb, ref, absacc, k, "mx_gemm %dx%dx%d" % (m, n, k))
@@ -160,7 +169,7 @@ def test_mx_full_size(cr, name, rotate):
     y = cr.mx_linear(xd, bc, bsc, rotate=rotate)
     torch.cuda.synchronize()
     rows = workloads.sample_rows(c.m, seed=c.seed)
-    g = dict(ac=gu.host(ac), asc=gu.host(asc), bc=gu.host(bc), bsc=gu.host(bsc),
+    g = dict(ac=gu.host(ac), asc=natural_scales(gu.host(asc)), bc=gu.host(bc), bsc=natural_scales(gu.host(bsc)),
              y=gu.host_bf16(y[torch.from_numpy(rows).cuda()]))
     del xd, wd, ac, asc, bc, bsc, y
     print("mx full size %s: oracle" % name, flush=True)
