@@ -349,18 +349,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_flash_kernel(
     auto step = [&](int kc, const uint8_t* st_k, const uint8_t* st_s, const uint8_t* st_v, bool do_pv,
                     const v16i (&s_cur)[2], v16i (&s_nxt)[2], const v8h (&p_prev)[2][2],
                     v8h (&p_cur)[2][2]) {
-        // Per-step fragment base addresses (9 per lane), kept opaque so that
-        // the compiler does not re-associate them with the slot arithmetic:
-        // each read is then base + the 32-row block offset as an immediate.
+        // Per-step fragment base addresses (9 per lane): the slots' LDS
+        // addresses are wave-uniform (scalar registers), one vector add each,
+        // kept opaque so that the compiler does not re-associate them with
+        // the slot arithmetic; each read is then base + the 32-row block
+        // offset as an immediate.
+        const uint32_t ak = __builtin_amdgcn_readfirstlane(lds_addr(st_k));
+        const uint32_t av = __builtin_amdgcn_readfirstlane(lds_addr(st_v));
+        const uint32_t as = __builtin_amdgcn_readfirstlane(lds_addr(st_s));
         uint32_t kbase[4], vbase[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            kbase[i] = lds_addr(st_k) + (uint32_t)k_lane[i];
-            vbase[i] = lds_addr(st_v) + (uint32_t)v_lane[i];
+            kbase[i] = ak + (uint32_t)k_lane[i];
+            vbase[i] = av + (uint32_t)v_lane[i];
             asm volatile("" : "+v"(kbase[i]));
             asm volatile("" : "+v"(vbase[i]));
         }
-        uint32_t sbase = lds_addr(st_s) + (uint32_t)(K_BYTES + V_BYTES + 16 * g);
+        uint32_t sbase = as + (uint32_t)(K_BYTES + V_BYTES + 16 * g);
         asm volatile("" : "+v"(sbase));
         auto kf_at = [&](int n) -> v4i {     // MFMA n of phase 1: kb = n & 1, s = n >> 1
             return *reinterpret_cast<const lds_v4i*>(lds_ptr(kbase[n >> 1] + 4096 * (n & 1)));
