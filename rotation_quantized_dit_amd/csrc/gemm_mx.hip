@@ -9,20 +9,26 @@
 //
 // Operands: codes [rows, K/2] bytes (element 2j in the low nibble of byte j)
 // and E8M0 scales chunk-major, [K/128][rows][4] bytes (the 4 block scales of
-// one 128-element chunk of consecutive rows are contiguous).  In bytes, a 64-element k-step of FP4
-// occupies 32 bytes of a row and each lane takes 16 of them (lanes 0-31 the
-// first 32 elements, lanes 32-63 the next 32), exactly the layout of the
-// int8 operands of K-GEMM; so the tiling below is that kernel's 256-row
-// variant: a 256 x 256 tile, 8 waves (two per SIMD) in a 4 x 2 grid of
-// 64 x 128 wave tiles, 64 bytes (128 elements) of K per stage through a
-// 4-slot LDS ring of direct buffer loads, XOR-swizzled 64-byte rows.
-// Each stage also carries one 32-bit word per tile row: the 4 block scales
-// of that row's 128 elements, copied by 4-byte direct loads (one per wave:
-// waves 0-3 the 256 A rows, waves 4-7 the 256 B rows), 256 contiguous bytes
-// per copy in the chunk-major layout (row-major scales would put each lane's
-// word in a different cache line, which measured 30 % slower).  For k-step s a lane
-// reads the one byte it needs, block 2 s + lane / 32 of its row, with a byte
-// load from LDS, so the scale operand needs no vector instruction.
+// one 128-element chunk of consecutive rows are contiguous).  In bytes, a
+// 64-element k-step of FP4 occupies 32 bytes of a row and each lane takes 16
+// of them (lanes 0-31 the first 32 elements, lanes 32-63 the next 32),
+// exactly the layout of the int8 operands of K-GEMM, so the tiling is that
+// kernel's: a 384 x 256 tile, 8 waves (two per SIMD) in a 4 x 2 grid of
+// 96 x 128 wave tiles (3 x 4 MFMA blocks, 192 fp32 accumulators per lane),
+// 64 bytes (128 elements) of K per stage through a 3-slot LDS ring of direct
+// buffer loads, XOR-swizzled 64-byte rows, one fragment set per k-step.
+// The 96 x 128 wave tile reads 7 fragments per 12 MFMAs (against 6 per 8
+// for 64 x 128) and the 384-row tile copies 17 % fewer bytes per flop than a
+// 256-row one; both measured about 8 % faster on the FFN-input shape.
+//
+// Each stage also carries the tile's scale words (one 32-bit word per row:
+// the 4 block scales of its 128 elements), 384 + 256 words copied as three
+// 1 KiB direct loads: waves 0 and 1 take the A rows (the upper half of wave
+// 1's copy reads rows past the tile into unused space), wave 2 the B rows.
+// So that the copy needs no branch, waves 3-7 issue the same load on an
+// empty buffer resource (every lane out of range: no memory is read) into a
+// spare 1 KiB of LDS.  For k-step s a lane reads the one byte it needs,
+// block 2 s + lane / 32 of its row, with a byte load from LDS.
 //
 // Ragged rows are clamped to the last row for loading and masked at the
 // store; K must be a multiple of 128.
@@ -35,7 +41,7 @@
 namespace convrot {
 namespace {
 
-constexpr int BM = 256;
+constexpr int BM = 384;
 constexpr int BN = 256;
 constexpr int BK = 64;                       // bytes of codes per row per stage (128 elements)
 constexpr int MA = BM / 128;                 // 32-row A blocks per wave
@@ -43,16 +49,19 @@ constexpr int NWAVES = 8;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int A_STAGE = BM * BK;
 constexpr int B_STAGE = BN * BK;
-constexpr int S_STAGE = 4 * (BM + BN);       // scale words
-constexpr int STAGE_BYTES = A_STAGE + B_STAGE + S_STAGE;
-constexpr int STAGES = 4;
-constexpr int COPIES = MA + 2 + 1;           // per wave per stage: A, B and one scale copy
+constexpr int SA_BYTES = 2048;               // 384 A scale words (+ the unused half of the second copy)
+constexpr int SB_BYTES = 1024;               // 256 B scale words
+constexpr int STAGE_BYTES = A_STAGE + B_STAGE + SA_BYTES + SB_BYTES;
+constexpr int STAGES = 3;
+constexpr int COPIES = MA + 3;               // per wave per stage: A, B and one scale copy
+constexpr int SPARE = STAGES * STAGE_BYTES;  // 1 KiB that the idle scale copies fill
 constexpr int PITCH = 136;
 constexpr int STASH_WAVE_BYTES = 32 * PITCH * 4;
 constexpr int STASH_BYTES = NWAVES * STASH_WAVE_BYTES;
 constexpr int RING_BYTES = STAGES * STAGE_BYTES;
 constexpr int LDS_BYTES = RING_BYTES > STASH_BYTES ? RING_BYTES : STASH_BYTES;
-constexpr int GROUP_M = 8;
+constexpr int GROUP_M = 4;                   // M-tiles per raster group
+static_assert(SPARE + 1024 <= LDS_BYTES, "spare area");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -70,8 +79,6 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-// Hardware barrier for the ring (copies completed by the preceding vmcnt
-// wait, this wave's LDS reads by lgkmcnt(0)).
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_waitcnt(0xC07F);
@@ -85,12 +92,6 @@ __device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* dst
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voff, soff, 0, 0);
 #endif
 }
-__device__ __forceinline__ void copy4(__amdgpu_buffer_rsrc_t rsrc, uint8_t* dst, uint32_t voff,
-                                      uint32_t soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 4, voff, soff, 0, 0);
-#endif
-}
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
@@ -100,8 +101,6 @@ struct Tile {
     int tm, tn;
 };
 
-// Tile ids dealt round-robin to the 8 XCDs are remapped so that each XCD
-// walks a contiguous range of a grouped raster (GROUP_M row tiles per group).
 __device__ __forceinline__ Tile map_tile(int b, int MT, int NT) {
     const int T = MT * NT;
     const int xcd = b & 7;
@@ -131,23 +130,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
     const int n0 = tile.tn * BN;
     const int rows_a = (M - m0) < BM ? (M - m0) : BM;
     const int rows_b = (N - n0) < BN ? (N - n0) : BN;
-    const int KB = K / 2;                    // code bytes per row
+    const int KB = K / 2;
+    const int KT = K / 128;
 
     const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(A + (int64_t)m0 * KB, (uint32_t)rows_a * (uint32_t)KB);
     const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(B + (int64_t)n0 * KB, (uint32_t)rows_b * (uint32_t)KB);
-    // scales of this tile's rows: chunk kt at byte kt * rows_total * 4 from
-    // the tile's first row (the resource spans every chunk of those rows)
-    const int KT_ = K / 128;
+    // scale copies: waves 0 and 1 the tile's A scale words (rows 256 w + 4 l .. +3; the upper half of
+    // wave 1's copy reads rows past the tile into the unused end of the A scale area), wave 2 the B
+    // words; waves 3-7 issue the same instruction on an empty resource into a spare area (no branch)
     const __amdgpu_buffer_rsrc_t rsrc_s =
-        wave < 4 ? make_rsrc(SA + (int64_t)m0 * 4, (uint32_t)((int64_t)(KT_ - 1) * M * 4 + rows_a * 4))
-                 : make_rsrc(SB + (int64_t)n0 * 4, (uint32_t)((int64_t)(KT_ - 1) * N * 4 + rows_b * 4));
-    const uint32_t chunk_stride = (uint32_t)(wave < 4 ? M : N) * 4u;
-
-    // Copy sources: copy i < MA of wave w fills A rows 16 (MA w + i) .. +15,
-    // copies MA, MA + 1 fill B rows 32 w + 16 (i - MA) .. +15 (lane l: row
-    // l / 4 of the 16, chunk position l % 4 holding logical chunk
-    // (l % 4) ^ swz(row)); the scale copy of wave w takes row 64 (w % 4) + l
-    // of A (waves 0-3) or B (waves 4-7).
+        wave < 2 ? make_rsrc(SA + (int64_t)m0 * 4, (uint32_t)((int64_t)(KT - 1) * M * 4 + rows_a * 4))
+        : wave == 2 ? make_rsrc(SB + (int64_t)n0 * 4, (uint32_t)((int64_t)(KT - 1) * N * 4 + rows_b * 4))
+                    : make_rsrc(SB, 0u);
+    const uint32_t chunk_stride = wave < 2 ? (uint32_t)M * 4u : wave == 2 ? (uint32_t)N * 4u : 0u;
+    const uint32_t voff_s = (uint32_t)(wave < 2 ? 1024 * wave : 0) + 16u * (uint32_t)lane;
+    const int s_dst = wave < 2 ? A_STAGE + B_STAGE + 1024 * wave
+                      : wave == 2 ? A_STAGE + B_STAGE + SA_BYTES : SPARE;
     uint32_t voff[MA + 2];
 #pragma unroll
     for (int i = 0; i < MA + 2; ++i) {
@@ -156,9 +154,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
         const int src_row = rr < lim ? rr : lim - 1;
         voff[i] = (uint32_t)src_row * (uint32_t)KB + 16u * (uint32_t)((lane & 3) ^ swz(rr));
     }
-    const int srow = 64 * (wave & 3) + lane;
-    const int slim = wave < 4 ? rows_a : rows_b;
-    const uint32_t voff_s = (uint32_t)(srow < slim ? srow : slim - 1) * 4u;
     auto issue = [&](int kt, int slot) {
         uint8_t* st = lds + slot * STAGE_BYTES;
         const uint32_t soff = (uint32_t)kt * BK;
@@ -166,14 +161,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
         for (int i = 0; i < MA; ++i) copy16(rsrc_a, st + 16 * 64 * MA * wave + 1024 * i, voff[i], soff);
         copy16(rsrc_b, st + A_STAGE + 32 * 64 * wave, voff[MA], soff);
         copy16(rsrc_b, st + A_STAGE + 32 * 64 * wave + 1024, voff[MA + 1], soff);
-        copy4(rsrc_s, st + A_STAGE + B_STAGE + 256 * wave, voff_s, (uint32_t)kt * chunk_stride);
+        copy16(rsrc_s, (wave < 3 ? st : lds) + s_dst, voff_s, (uint32_t)kt * chunk_stride);
     };
-
-    int a_row[MA], b_row[4];
-#pragma unroll
-    for (int a = 0; a < MA; ++a) a_row[a] = 32 * MA * wm + 32 * a + (lane & 31);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) b_row[b] = 128 * wn + 32 * b + (lane & 31);
 
     v16f acc[MA][4];
 #pragma unroll
@@ -183,35 +172,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
 
-    int a_off[2][MA], b_off[2][4];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const int c = 2 * s + g;
-#pragma unroll
-        for (int a = 0; a < MA; ++a) a_off[s][a] = a_row[a] * BK + 16 * (c ^ swz(a_row[a]));
-#pragma unroll
-        for (int b = 0; b < 4; ++b) b_off[s][b] = A_STAGE + b_row[b] * BK + 16 * (c ^ swz(b_row[b]));
-    }
-    // Byte offsets (within a stage) of this lane's scale bytes for k-step s:
-    // block 2 s + g of the lane's A rows and B rows.
-    int sa_off[2][MA], sb_off[2][4];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-#pragma unroll
-        for (int a = 0; a < MA; ++a) sa_off[s][a] = A_STAGE + B_STAGE + 4 * a_row[a] + 2 * s + g;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) sb_off[s][b] = A_STAGE + B_STAGE + 4 * BM + 4 * b_row[b] + 2 * s + g;
-    }
-    // Fragments and scale bytes of k-step s of a stage.
+    // Per-lane byte offsets within a stage.  The swizzle of every fragment
+    // row of a lane is (lane >> 2) & 3 (the rows differ by multiples of 32),
+    // so each operand needs one lane offset per k-step, the blocks following
+    // at fixed distances (2048 bytes per 32 code rows, 128 per 32 scale words).
+    const int sw = (lane >> 2) & 3;
+    const int a_lane = (32 * MA * wm + (lane & 31)) * BK;
+    const int b_lane = A_STAGE + (128 * wn + (lane & 31)) * BK;
+    const int sa_lane = A_STAGE + B_STAGE + 4 * (32 * MA * wm + (lane & 31)) + g;
+    const int sb_lane = A_STAGE + B_STAGE + SA_BYTES + 4 * (128 * wn + (lane & 31)) + g;
     auto read_frags = [&](const uint8_t* st, int s, v4i (&af)[MA], v4i (&bf)[4], int (&sa)[MA], int (&sb)[4]) {
+        const int c = 16 * ((2 * s + g) ^ sw);
+        const uint8_t* pa = st + (a_lane + c);
+        const uint8_t* pb = st + (b_lane + c);
 #pragma unroll
-        for (int a = 0; a < MA; ++a) af[a] = *reinterpret_cast<const v4i*>(st + a_off[s][a]);
+        for (int a = 0; a < MA; ++a) af[a] = *reinterpret_cast<const v4i*>(pa + 2048 * a);
 #pragma unroll
-        for (int b = 0; b < 4; ++b) bf[b] = *reinterpret_cast<const v4i*>(st + b_off[s][b]);
+        for (int b = 0; b < 4; ++b) bf[b] = *reinterpret_cast<const v4i*>(pb + 2048 * b);
+        const uint8_t* psa = st + sa_lane;
+        const uint8_t* psb = st + sb_lane;
 #pragma unroll
-        for (int a = 0; a < MA; ++a) sa[a] = st[sa_off[s][a]];
+        for (int a = 0; a < MA; ++a) sa[a] = psa[128 * a + 2 * s];
 #pragma unroll
-        for (int b = 0; b < 4; ++b) sb[b] = st[sb_off[s][b]];
+        for (int b = 0; b < 4; ++b) sb[b] = psb[128 * b + 2 * s];
     };
     auto mma = [&](const v4i (&af)[MA], const v4i (&bf)[4], const int (&sa)[MA], const int (&sb)[4]) {
 #pragma unroll
@@ -225,92 +208,55 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
             }
     };
 
-    static_assert(MA == 2 && COPIES == 5, "the interleave patterns below count 8 MFMAs, 12 reads, 5 copies");
-    const int KT = K / 128;
-    // conditional prologue and branchy wait, as in K-GEMM (an unconditional
-    // one makes the compiler drain the ring before every stage's first read)
 #pragma unroll
     for (int st = 0; st < STAGES; ++st)
         if (st < KT) issue(st, st);
     {
         const int ahead = (KT - 1) < (STAGES - 1) ? (KT - 1) : (STAGES - 1);
-        if (ahead >= 3) wait_vmcnt<3 * COPIES>();
-        else if (ahead >= 2) wait_vmcnt<2 * COPIES>();
+        if (ahead >= 2) wait_vmcnt<2 * COPIES>();
         else if (ahead == 1) wait_vmcnt<COPIES>();
         else wait_vmcnt<0>();
     }
     lds_barrier();
 
-    // Software pipeline (as K-GEMM's 256-row variant): in stage kt, k-step 0
-    // runs on register set 0 while k-step 1's operands are read into set 1;
-    // after the barrier, k-step 1 runs on set 1 while the slot is refilled
-    // with stage kt + STAGES and stage kt + 1's k-step 0 is read into set 0.
-    int kt = 0;
     int slot = 0;
-    v4i fa0[MA], fb0[4], fa1[MA], fb1[4];
-    int sa0[MA], sb0[4], sa1[MA], sb1[4];
-    read_frags(lds, 0, fa0, fb0, sa0, sb0);
+    int kt = 0;
+    v4i fa[MA], fb[4];
+    int sa[MA], sb[4];
+    // Steady state (a refill per stage) as straight-line code, so that the
+    // scheduling barriers hold the order: k-step 0's reads and MFMAs, k-step
+    // 1's reads, the wait for stage kt + 1 and the barrier, the refill, k-step
+    // 1's MFMAs.
     for (; kt + STAGES < KT; ++kt) {
         const int next = slot + 1 == STAGES ? 0 : slot + 1;
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1, sa1, sb1);
-        mma(fa0, fb0, sa0, sb0);
-        // 8 MFMAs, 12 LDS reads (6 fragments, 6 scale bytes)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
-        }
-#pragma unroll
-        for (int i = 4; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+        read_frags(lds + slot * STAGE_BYTES, 0, fa, fb, sa, sb);
+        mma(fa, fb, sa, sb);
         __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<(STAGES - 2) * COPIES>();
+        read_frags(lds + slot * STAGE_BYTES, 1, fa, fb, sa, sb);
+        wait_vmcnt<COPIES>();
         lds_barrier();
         __builtin_amdgcn_sched_barrier(0);
-        read_frags(lds + next * STAGE_BYTES, 0, fa0, fb0, sa0, sb0);
         issue(kt + STAGES, slot);
-        mma(fa1, fb1, sa1, sb1);
-        // 8 MFMAs, 12 LDS reads and the 5 copies of the refill
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // two LDS reads
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one direct copy
-        }
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
-#pragma unroll
-        for (int i = 5; i < 8; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        }
+        mma(fa, fb, sa, sb);
         __builtin_amdgcn_sched_barrier(0);
         slot = next;
     }
-    for (; kt + 1 < KT; ++kt) {
+    for (; kt < KT; ++kt) {
         const int next = slot + 1 == STAGES ? 0 : slot + 1;
-        read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1, sa1, sb1);
-        mma(fa0, fb0, sa0, sb0);
-        const int after = KT - 2 - kt;
-        if (after >= 2) wait_vmcnt<2 * COPIES>();
-        else if (after >= 1) wait_vmcnt<COPIES>();
-        else wait_vmcnt<0>();
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(lds + slot * STAGE_BYTES, 0, fa, fb, sa, sb);
+        mma(fa, fb, sa, sb);
+        __builtin_amdgcn_sched_barrier(0);
+        read_frags(lds + slot * STAGE_BYTES, 1, fa, fb, sa, sb);
+        wait_vmcnt<0>();
         lds_barrier();
-        read_frags(lds + next * STAGE_BYTES, 0, fa0, fb0, sa0, sb0);
-        mma(fa1, fb1, sa1, sb1);
+        __builtin_amdgcn_sched_barrier(0);
+        mma(fa, fb, sa, sb);
+        __builtin_amdgcn_sched_barrier(0);
         slot = next;
     }
-    read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1, sa1, sb1);
-    mma(fa0, fb0, sa0, sb0);
-    mma(fa1, fb1, sa1, sb1);
 
-    // Epilogue: each wave parks a 32 x 128 block of fp32 accumulators in its
-    // part of the freed ring and writes it back as bf16, 8 consecutive columns
-    // of one row per lane per 16-byte store.
     lds_barrier();
     float* stash = reinterpret_cast<float*>(lds + wave * STASH_WAVE_BYTES);
     const int grow0 = m0 + 32 * MA * wm;
