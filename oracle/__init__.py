@@ -71,6 +71,7 @@ def lib() -> ctypes.CDLL:
         L.orc_silu.argtypes = [ctypes.c_float]
         L.orc_silu.restype = ctypes.c_float
         L.orc_swiglu_bf16.argtypes = [P, I64, I64, P, P, P]
+        L.orc_swiglu_ref.argtypes = [P, I64, I64, P, P, P, P]
         L.orc_swiglu_pairs_bf16.argtypes = [P, I64, I64, P]
         L.orc_swiglu_rotate_quant_rows.argtypes = [P, I64, P, I64, P, P]
         L.orc_swiglu_rotate_quant_rows.restype = ctypes.c_int
@@ -236,6 +237,22 @@ def swiglu_bf16(acc: np.ndarray, s_x: np.ndarray, s_w: np.ndarray) -> np.ndarray
     return y
 
 
+def swiglu_ref(acc: np.ndarray, s_x: np.ndarray, s_w: np.ndarray):
+    """The exact fused-epilogue value in fp64, ref = silu(g) * u with g, u the
+    fp32 dequantized gate and up values (columns [0, i) and [i, 2i)); returns
+    (ref [m, i] float64, |g u| [m, i] float64)."""
+    acc = np.ascontiguousarray(acc, dtype=np.int32)
+    s_x = np.ascontiguousarray(s_x, dtype=np.float32)
+    s_w = np.ascontiguousarray(s_w, dtype=np.float32)
+    nrows, n2 = acc.shape
+    assert n2 % 2 == 0 and s_w.size == n2 and s_x.size == nrows
+    i = n2 // 2
+    ref = np.empty((nrows, i), np.float64)
+    mag = np.empty((nrows, i), np.float64)
+    lib().orc_swiglu_ref(_p(acc), nrows, i, _p(s_x), _p(s_w), _p(ref), _p(mag))
+    return ref, mag
+
+
 def swiglu_pairs_bf16(gu_bf16: np.ndarray) -> np.ndarray:
     """h = bf16(silu(g) * u) from fc1's bf16 output [m, 2i]: g = columns
     [0, i), u = columns [i, 2i), both widened exactly."""
@@ -308,10 +325,18 @@ def linear_rows(x_bf16, q_w, s_w, rows=None):
 
 
 def linear_swiglu_rows(x_bf16, q_w, s_w, rows=None):
-    """y rows of the ConvRot fc1 with fused SwiGLU (q_w holds 2i rows)."""
+    """y rows of the ConvRot fc1 with fused SwiGLU (q_w holds 2i rows), with
+    the oracle's fixed fp32 exponential, rounded to bf16."""
     qx, sx = rotate_quant_act(x_bf16, rows)
     acc = gemm_s32(qx, q_w)
     return swiglu_bf16(acc, sx, s_w)
+
+
+def linear_swiglu_ref_rows(x_bf16, q_w, s_w, rows=None):
+    """The exact fused fc1 value for the given rows: (ref, |g u|), see swiglu_ref."""
+    qx, sx = rotate_quant_act(x_bf16, rows)
+    acc = gemm_s32(qx, q_w)
+    return swiglu_ref(acc, sx, s_w)
 
 
 # ------------------------------------------------------------------ attention

@@ -318,6 +318,30 @@ void orc_swiglu_bf16(const int32_t* acc, int64_t nrows, int64_t i_width, const f
     }
 }
 
+/* The exact value the fused fc1 epilogue approximates (h3-rs README,
+ * "Speed": SwiGLU fused into the GEMM epilogue; the layer's contract checks
+ * its bf16 output against the exact result within a relative bound, and
+ * requires bit equality only of codes, scales and integer accumulators).
+ * g and u are the fp32 dequantized gate and up values exactly as in
+ * orc_dequant_one (that step is part of the definition); then, in fp64 with
+ * libm's exp, ref = g / (1 + e^(-g)) * u, with no rounding to bf16.  mag
+ * receives |g * u|, the scale of an absolute floor where the quotient leaves
+ * the fp32 normal range.  acc has 2i columns per row; s_w has 2i entries. */
+void orc_swiglu_ref(const int32_t* acc, int64_t nrows, int64_t i_width, const float* s_x, const float* s_w,
+                    double* ref, double* mag) {
+    int64_t j;
+#pragma omp parallel for schedule(static)
+    for (j = 0; j < nrows; ++j) {
+        for (int64_t c = 0; c < i_width; ++c) {
+            const double g = (double)orc_dequant_one(acc[j * 2 * i_width + c], s_x[j], s_w[c]);
+            const double u =
+                (double)orc_dequant_one(acc[j * 2 * i_width + i_width + c], s_x[j], s_w[i_width + c]);
+            ref[j * i_width + c] = g / (1.0 + exp(-g)) * u;
+            mag[j * i_width + c] = fabs(g * u);
+        }
+    }
+}
+
 /* --------------------------------------------- SwiGLU on fc1's output side */
 
 /* SwiGLU placed on the output side of fc1 (hybrid model card, "Native NVFP4

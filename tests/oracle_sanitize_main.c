@@ -39,6 +39,8 @@ float orc_exp(float x);
 float orc_silu(float g);
 void orc_swiglu_bf16(const int32_t* acc, int64_t nrows, int64_t i_width, const float* s_x, const float* s_w,
                      uint16_t* y);
+void orc_swiglu_ref(const int32_t* acc, int64_t nrows, int64_t i_width, const float* s_x, const float* s_w,
+                    double* ref, double* mag);
 void orc_swiglu_pairs_bf16(const uint16_t* gu, int64_t nrows, int64_t i_width, uint16_t* h);
 int orc_swiglu_rotate_quant_rows(const uint16_t* gu, int64_t i_width, const int64_t* rows, int64_t nrows,
                                  int8_t* q, float* s);
@@ -176,6 +178,10 @@ static void test_gemm_and_epilogues(void) {
     (void)orc_dequant_one(-2147483647 - 1, 1e-45f, -1e-45f);
     uint16_t* ys = xmalloc(sizeof(uint16_t) * m * iw);
     orc_swiglu_bf16(acc, m, iw, sx, sw, ys);
+    double* ref = xmalloc(sizeof(double) * m * iw);
+    double* mag = xmalloc(sizeof(double) * m * iw);
+    orc_swiglu_ref(acc, m, iw, sx, sw, ref, mag);
+    free(ref); free(mag);
     const float xs[] = {-1e30f, -200.0f, -88.0f, -86.0f, -1.0f, -0.0f, 0.0f, 1.0f, 80.0f, 88.72f, 89.0f,
                         1e30f, INFINITY, -INFINITY, NAN};
     for (size_t i = 0; i < sizeof xs / sizeof xs[0]; ++i) {

@@ -386,6 +386,70 @@ def test_swiglu_epilogue_layout_and_value():
     assert not np.allclose(y, swapped, rtol=1e-2)
 
 
+def test_swiglu_ref_layout_and_value():
+    """The fp64 reference of the fused epilogue takes g from the first half of
+    the columns and u from the second, each the fp32 dequant (a value within
+    two fp32 roundings of acc s_x s_w), and returns silu(g) u unrounded: against
+    an fp64 evaluation on the exact products it differs by at most the fp32
+    dequant's rounding; |g u| comes back as the magnitude."""
+    rng = np.random.default_rng(29)
+    i = 40
+    acc = rng.integers(-3_000_000, 3_000_000, (6, 2 * i)).astype(np.int32)
+    sx = rng.uniform(0.01, 0.1, 6).astype(np.float32)
+    sw = rng.uniform(1e-5, 1e-4, 2 * i).astype(np.float32)
+    ref, mag = oracle.swiglu_ref(acc, sx, sw)
+    g = acc[:, :i] * sx.astype(np.float64)[:, None] * sw[:i].astype(np.float64)
+    u = acc[:, i:] * sx.astype(np.float64)[:, None] * sw[i:].astype(np.float64)
+    exact = g / (1 + np.exp(-g)) * u
+    # g and u carry relative errors <= 2U each (two fp32 roundings); a relative
+    # error e in g moves silu(g) by |1 + g (1 - sigma(g))| e relatively, so
+    # the propagated bound is (|1 + g (1 - sigma(g))| + 1) 2U (+ a margin)
+    sig = 1 / (1 + np.exp(-g))
+    amp = np.abs(1 + g * (1 - sig)) + 1
+    assert np.all(np.abs(ref - exact) <= 2.2 * U * amp * np.abs(exact) + 1e-300)
+    assert np.allclose(mag, np.abs(g * u), rtol=8 * U)
+    swapped = u / (1 + np.exp(-u)) * g
+    assert not np.allclose(ref, swapped, rtol=1e-2)
+
+
+def test_swiglu_ref_closed_forms():
+    """sigma(ln 3) = 3/4 and sigma(-ln 3) = 1/4, so silu(+-ln 3) = +-ln 3 * 3/4,
+    -ln 3 / 4; silu(g) - silu(-g) = g for any g; e^-g vanishes for large g
+    (silu(g) = g) and overflows for very negative g (silu(g) = -0)."""
+    ln3 = np.float32(math.log(3.0))
+    acc = np.array([[1, -1, 1, 0, 7, 5, 1, 1, 1, 1, 1, 1]], np.int32)
+    sx = np.ones(1, np.float32)
+    sw = np.array([ln3, ln3, 100.0, 1.0, -200.0, 3.0, 1.0, 1.0, 2.5, 1.0, 1.0, 1.0], np.float32)   # g | u
+    ref, mag = oracle.swiglu_ref(acc, sx, sw)
+    g = float(ln3)
+    d = g - math.log(3.0)            # fp32 rounding of ln 3, |d| < 2^-24 ln 3
+    # sigma(ln 3 + d) = 3/4 + (3/16) d + O(d^2), sigma(-ln 3 - d) = 1/4 - (3/16) d + O(d^2)
+    assert abs(ref[0, 0] - g * (0.75 + 3 / 16 * d)) <= 1e-15
+    assert abs(ref[0, 1] - (-g) * (0.25 - 3 / 16 * d)) <= 1e-15
+    assert abs((ref[0, 0] - ref[0, 1]) - g) <= 1e-15
+    assert ref[0, 2] == 100.0 * 2.5                 # silu(100) = 100 to fp64 precision, u = 2.5
+    assert ref[0, 3] == 0.0                         # silu(0) = 0
+    assert ref[0, 4] == 0.0 and math.copysign(1.0, ref[0, 4]) < 0   # g = -1400: e^1400 overflows
+    assert mag[0, 4] == 1400.0 * 1.0
+    assert abs(ref[0, 5] - 15.0 / (1 + math.exp(-15.0))) <= 1e-13
+
+
+def test_swiglu_ref_agrees_with_fixed_fp32_path():
+    """Two independent evaluations: the fp64 reference rounded once to bf16
+    and the oracle's fixed fp32 exponential path agree within one bf16 ulp on
+    every element, and exactly on all but a small fraction."""
+    rng = np.random.default_rng(31)
+    i = 512
+    acc = rng.integers(-4_000_000, 4_000_000, (16, 2 * i)).astype(np.int32)
+    sx = rng.uniform(0.005, 0.05, 16).astype(np.float32)
+    sw = rng.uniform(1e-5, 2e-4, 2 * i).astype(np.float32)
+    ref, _ = oracle.swiglu_ref(acc, sx, sw)
+    fixed = hd.bf16_bits_to_f64(oracle.swiglu_bf16(acc, sx, sw))
+    ref_b = hd.bf16_bits_to_f64(workloads.to_bf16_bits(ref.astype(np.float32)))
+    assert np.all(np.abs(fixed - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+    assert np.mean(fixed != ref_b) < 0.01
+
+
 # ------------------------------------------------------------------ method level
 
 def _rel_fro(y_bits, exact):
