@@ -31,13 +31,22 @@
  *   contract   acc[m][n] = sum_k q_x[m][k] * q_w[n][k] (exact int32);
  *   dequant    y = bf16_rne(((float)acc * s_x[m]) * s_w[n]);
  *   SwiGLU     g, u = the fp32 dequant of gate column j and up column i + j;
- *              y = bf16_rne(silu(g) * u), silu(g) = g / (1 + exp(-g)) with one
- *              fixed fp32 exp (Cody-Waite reduction with ln2 split into
- *              0x1.62e4p-1 + 0x1.7f7d1cp-20, k = rint(x * 0x1.715476p+0), degree-7
- *              Taylor polynomial in Horner form with fused multiply-adds, scaled
- *              by 2^k; exp(x) = +inf for x > 88.72 and 0 for x < -86).
- * All results are bit-reproducible: the same inputs give the same bytes on
- * every call, launch shape and device of this architecture.
+ *              y = bf16_rne(silu(g) * u), silu(g) = g / (1 + exp(-g)), in the
+ *              fused epilogue evaluated on the transcendental unit as
+ *              (g * rcp(1 + exp2(-g * log2 e))) * u: y lies within 2^-8 |y|
+ *              of the exact value (one bf16 rounding plus ~1.2e-5 relative
+ *              from the fp32 evaluation), or within |g u| 2^-126 where
+ *              1 + e^-g exceeds 2^126.
+ *   fixed exp  the output-side SwiGLU pass (convrot_swiglu_rotate_quant_act),
+ *              whose h decides int8 codes, uses one fixed fp32 exp instead
+ *              (Cody-Waite reduction with ln2 split into 0x1.62e4p-1 +
+ *              0x1.7f7d1cp-20, k = rint(x * 0x1.715476p+0), degree-7 Taylor
+ *              polynomial in Horner form with fused multiply-adds, scaled by
+ *              2^k; exp(x) = +inf for x > 88.72 and 0 for x < -86) and one IEEE
+ *              division, so that its codes are reproducible bit for bit.
+ * All results are deterministic: the same inputs give the same bytes on every
+ * call, launch shape and device of this architecture; every result except
+ * the fused SwiGLU output is the definition's rounding sequence bit for bit.
  *
  * Conventions for every entry point:
  *   - All array pointers are DEVICE pointers, owned by the caller.  The library
@@ -102,7 +111,7 @@ int convrot_rotate_quant_act(const uint16_t* x, int64_t m, int64_t k,
  * "Native NVFP4 projection benchmarks": an "FFN output + SwiGLU" projection).
  * fc1 writes its dequantized gate and up columns as bf16 (convrot_linear with
  * n = 2i); this pass forms h = bf16(silu(g) * u), silu(g) = g / (1 + exp(-g))
- * with the same fixed exponential as the SwiGLU epilogue, widens h exactly,
+ * with the fixed exponential and one IEEE division, widens h exactly,
  * and rotates and quantizes it per token as convrot_rotate_quant_act does.
  *   gu   [m, 2i] bf16: columns [0, i) gate, columns [i, 2i) up
  *   q_h  [m, i]  int8 output codes;  s_h [m] fp32 output per-token scales
@@ -134,7 +143,8 @@ int convrot_linear(const uint16_t* x, int64_t m, int64_t k,
  *              rows [i, 2i) the up projection (quantize the whole [2i, k]
  *              weight with convrot_quantize_weight; scales are per row, so this
  *              equals quantizing the halves separately)
- *   y          [m, i] bf16 output silu(gate) * up                            */
+ *   y          [m, i] bf16 output silu(gate) * up, within 2^-8 |y| of the
+ *              exact value (the SwiGLU line of the arithmetic above)          */
 int convrot_linear_swiglu(const uint16_t* x, int64_t m, int64_t k,
                           const int8_t* q_w, const float* s_w, int64_t i,
                           uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);

@@ -1,5 +1,6 @@
-// Device arithmetic shared by the GEMM epilogues and the rotate+quantize
-// passes, evaluated op for op as the layer's definition fixes it.
+// Device arithmetic of the GEMM epilogues and the rotate+quantize passes
+// that must be reproducible bit for bit, evaluated op for op as the layer's
+// definition fixes it.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -47,7 +48,8 @@ __device__ __forceinline__ float one_plus_exp_cw(float x) {
 }
 
 // silu(g) * u with silu(g) = g / (1 + exp(-g)) (one IEEE division), before
-// any bf16 rounding.
+// any bf16 rounding: the output-side SwiGLU pass, whose h feeds the int8
+// quantizer, so that its codes are reproducible bit for bit.
 __device__ __forceinline__ float swiglu_f32(float g, float u) {
     return (g / one_plus_exp_cw(-g)) * u;
 }

@@ -10,7 +10,9 @@
 //   BF16   : y[m][n] = bf16_rne(((float)acc * s_x[m]) * s_w[n])
 //   SWIGLU : g = fp32 dequant of column j, u = of column i + j (weight rows
 //            [0, i) are the gate, [i, 2i) the up projection);
-//            y[m][j] = bf16_rne(silu(g) * u), silu(g) = g / (1 + exp(-g)).
+//            y[m][j] = bf16_rne(silu(g) * u), silu(g) = g / (1 + exp(-g)),
+//            evaluated with the hardware base-2 exponential and reciprocal
+//            (see swiglu_hw).
 //
 // Tiling.  A workgroup of 8 waves (two per SIMD) owns a BM x 256 tile of acc
 // (BM tokens; for SwiGLU 128 gate columns + the matching 128 up columns).
@@ -141,6 +143,22 @@ __device__ __forceinline__ float dequant(int acc, float sx, float sw) {
     float f = (float)acc;
     f = f * sx;
     return f * sw;
+}
+
+// silu(g) * u for the fused epilogue, on the transcendental unit:
+// e = v_exp_f32(-g log2(e)), then (g * v_rcp_f32(1 + e)) * u.  Its result is a
+// bf16 output, which the layer's contract bounds relative to the exact value:
+// the argument's rounding moves e by at most |g log2 e| 2^-23 ln 2 (< 1.1e-5
+// relative for |g log2 e| < 128; beyond that e is 0 or +inf and the result is
+// g u or -0), the exponential and the reciprocal are each within 1 ulp, so
+// the fp32 result is within about 1.2e-5 of silu(g) u relatively and the bf16
+// result within one bf16 ulp (2^-8) of it.  Where 1 + e exceeds 2^126 the
+// reciprocal may flush to zero, a result below |g u| 2^-126 in magnitude.
+// (The output-side SwiGLU pass, whose silu decides int8 codes, keeps the
+// fixed exponential of fixed_math.h so that those codes match bit for bit.)
+__device__ __forceinline__ float swiglu_hw(float g, float u) {
+    const float e = __builtin_amdgcn_exp2f(g * -0x1.715476p+0f);
+    return (g * __builtin_amdgcn_rcpf(1.0f + e)) * u;
 }
 
 struct Tile {
@@ -456,7 +474,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                 for (int e = 0; e < 8; ++e) {
                     const float g = dequant(ga[e], sxr, swa[e]);
                     const float u = dequant(ua[e], sxr, swb[e]);
-                    h[e] = swiglu_f32(g, u);
+                    h[e] = swiglu_hw(g, u);
                 }
                 const v4u pk = {pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]), pack_bf16(h[4], h[5]),
                                 pack_bf16(h[6], h[7])};
