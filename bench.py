@@ -358,7 +358,26 @@ def main():
     cal2 = torch.empty_like(cal)
     cal2.copy_(cal)
     torch.cuda.synchronize()
-    del cal, cal2
+    # The same copy timed, and torch's elementwise kernel reading and writing
+    # the same bytes (1 GiB moved each): the streaming bandwidth a plain kernel
+    # reaches on this device, next to the 8 TB/s peak.
+    def timed(fn, reps=5):
+        fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * reps)]
+        for r in range(reps):
+            ev[2 * r].record()
+            fn()
+            ev[2 * r + 1].record()
+        torch.cuda.synchronize()
+        return float(np.median([ev[2 * r].elapsed_time(ev[2 * r + 1]) for r in range(reps)]))
+    calf, calf2 = cal.view(torch.float32), cal2.view(torch.float32)
+    copy_moved = 2.0 * cal.numel()
+    device_copy = {"bytes_moved": copy_moved,
+                   "memcpy_GB/s": round(copy_moved / (timed(lambda: cal2.copy_(cal)) * 1e-3) / 1e9, 1),
+                   "elementwise_GB/s": round(copy_moved / (timed(lambda: torch.mul(calf, 1.0, out=calf2)) * 1e-3)
+                                             / 1e9, 1)}
+    copy_gbs = max(device_copy["memcpy_GB/s"], device_copy["elementwise_GB/s"])
+    del cal, cal2, calf, calf2
 
     # load-time weight quantization (timed on its own)
     qwu, swu = cr.quantize_weight(wu)
@@ -445,6 +464,7 @@ def main():
             b = rot1_b if j == 0 else rot2_b
             e["GB/s"] = round(b / (d * 1e-3) / 1e9, 1)
             e["pct_hbm_peak"] = round(100.0 * b / (d * 1e-3) / 1e9 / PEAK_HBM_GBS, 1)
+            e["pct_of_device_copy"] = round(100.0 * b / (d * 1e-3) / 1e9 / copy_gbs, 1)
         else:
             o = ops_up if j == 1 else ops_dn
             e["TOPS"] = round(o / (d * 1e-3) / 1e12, 1)
@@ -571,6 +591,7 @@ def main():
         "fused_api_ms_per_step": round(fused_ms, 4),
         "output_side_swiglu": out_side,
         "weight_quant": {"ms": round(wq_ms, 4), "GB/s": round(wq_bytes / (wq_ms * 1e-3) / 1e9, 1)},
+        "device_copy": device_copy,
         "lora_merge_ffn_up": {"ms": round(merge_ms, 4), "rank": lr,
                               "GB/s": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1),
                               "note": "dequantize + rank-32 delta + requantize of the 28672 x 5376 weight, "
