@@ -118,31 +118,52 @@ struct SwiGluRows {
     }
 };
 
-__device__ __forceinline__ int quant_one(float v_un, float r16, float s, bool exact_all) {
-    float p = v_un * r16;
-    float n = __builtin_rintf(p);
-    if (exact_all || __builtin_fabsf(p - n) > 0.5f - 0x1p-14f) {
-        n = __builtin_rintf((v_un * 0.0625f) / s);
-        n = __builtin_fminf(__builtin_fmaxf(n, -127.0f), 127.0f);
-    }
-    return (int)n;
+// The exact path of one element: rint of the correctly rounded quotient
+// (v_un / 16 is exact), saturated at +-127.
+__device__ __forceinline__ float quant_exact(float v_un, float s) {
+    const float n = __builtin_rintf((v_un * 0.0625f) / s);
+    return __builtin_fminf(__builtin_fmaxf(n, -127.0f), 127.0f);
 }
 
 // Quantize one slot's 16 rotated values (elements j + 16 b) and store the
 // group's 256 codes in natural order: bytes are staged in the slot's tile and
 // read back as one 16-byte chunk per lane (elements 16 j .. 16 j + 15).
+// Eight values at a time, the fast products are rounded first; only when one
+// of the eight lies within 2^-14 of a half-integer (or the row's scale is
+// tiny) does the lane enter the exact path, and there each element makes the
+// same test, so every code is rint(RN(v / s)) whichever path it took.  (Eight
+// rather than sixteen keeps the rounded values of one half in registers
+// without lowering occupancy.)
 __device__ __forceinline__ void quant_store(float* tile, int j, const float t[16], float r16,
                                             float s, bool zero, bool exact_all, bool ok,
                                             int8_t* __restrict__ dst) {
-    uint8_t* cb = reinterpret_cast<uint8_t*>(tile);
+    uint8_t* cb = reinterpret_cast<uint8_t*>(tile) + j;
 #pragma unroll
-    for (int b = 0; b < 16; ++b) {
-        const int c = zero ? 0 : quant_one(t[b], r16, s, exact_all);
-        cb[b * 16 + j] = (uint8_t)(int8_t)c;
+    for (int h = 0; h < 16; h += 8) {
+        float n[8];
+        float dev = 0.0f;
+#pragma unroll
+        for (int b = 0; b < 8; ++b) {
+            const float p = t[h + b] * r16;
+            n[b] = __builtin_rintf(p);
+            dev = __builtin_fmaxf(dev, __builtin_fabsf(p - n[b]));
+        }
+        if (zero) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b) n[b] = 0.0f;
+        } else if (exact_all || dev > 0.5f - 0x1p-14f) {
+#pragma unroll
+            for (int b = 0; b < 8; ++b) {
+                const float p = t[h + b] * r16;
+                if (exact_all || __builtin_fabsf(p - n[b]) > 0.5f - 0x1p-14f) n[b] = quant_exact(t[h + b], s);
+            }
+        }
+#pragma unroll
+        for (int b = 0; b < 8; ++b) cb[(h + b) * 16] = (uint8_t)(int8_t)(int)n[b];
     }
     wave_fence();
     if (ok) {
-        const v4u c16 = *reinterpret_cast<const v4u*>(cb + j * 16);
+        const v4u c16 = *reinterpret_cast<const v4u*>(cb - j + j * 16);
         *reinterpret_cast<v4u*>(dst + j * 16) = c16;
     }
     wave_fence();
