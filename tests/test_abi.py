@@ -246,3 +246,16 @@ def test_mx_validation(L):
     assert L.convrot_mx_linear(A, 10, 512, 0, B, C, 4, D, MIS, need, None) == ERR_ALIGN
     assert L.convrot_mx_linear(A, 10, 384, 1, B, C, 4, D, D, need, None) == ERR_SHAPE
     assert L.convrot_mx_linear(None, 0, 512, 0, None, None, 4, None, None, 0, None) == OK
+
+
+@pytest.mark.parametrize("lang", ["c", "c++"])
+def test_header_compiles_as_c_and_cpp(lang):
+    """include/convrot.h stands alone as C99 and as C++17, warnings as errors."""
+    from tests import c_abi_build
+    c_abi_build.compile_only("c-header" if lang == "c" else "c++")
+
+
+def test_c_abi_check_source_compiles():
+    """tests/c_abi_check.c (the C-side check run on the GPU) is valid C11."""
+    from tests import c_abi_build
+    c_abi_build.compile_only("c")
