@@ -377,7 +377,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_flash_kernel(
             return *reinterpret_cast<const lds_v8h*>(
                 lds_ptr(vbase[2 * (n >> 3) + ((n >> 2) & 1)] + 4096 * (n & 3)));
         };
-        // ---- phase 1
+        // ---- phase 1 (at raised wave priority: while one wave of a SIMD
+        // issues its logits MFMAs, the other's softmax fills the gaps)
+        __builtin_amdgcn_s_setprio(1);
         v4i kf[8];
         v4f skv[8];
         float t[2][16];
@@ -407,6 +409,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_flash_kernel(
                 for (int r = 0; r < 16; ++r)
                     if (32 * kb + 8 * (r >> 2) + 4 * g + (r & 3) >= nvalid) t[kb][r] = -__builtin_inff();
         }
+        __builtin_amdgcn_s_setprio(0);
         // ---- phase 2
         constexpr int VD = 4;                        // V^T fragment prefetch distance
         v8h vf[16];
