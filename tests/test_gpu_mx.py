@@ -185,3 +185,34 @@ def test_mx_full_size(cr, name, rotate):
     gu.assert_equal(g["bsc"], obs, name + " weight scales")
     ref, absacc = oracle.mx_gemm(oac[rows], oas[rows], obc, obs)
     assert_mx_product(g["y"], ref, absacc, c.k, name + " sampled rows")
+
+
+@pytest.mark.parametrize("rotate", [False, True])
+def test_mx_max_k(cr, rotate):
+    """The largest K the MXFP4 entry points accept (2^20): every code and scale
+    of 3 activation and 5 weight rows bit for bit, and the product within its
+    bound (the fp32 accumulation term grows with k / 32)."""
+    import torch
+    k = 1 << 20
+    rng = np.random.default_rng(77)
+    x = rng.standard_normal((3, k)).astype(np.float32)
+    x[:, rng.choice(k, 64, replace=False)] *= 30
+    w = (0.02 * rng.standard_normal((5, k))).astype(np.float32)
+    xb = workloads.to_bf16_bits(x)
+    xd, wd = gu.dev_bf16(xb), gu.dev(w)
+    ac, asc = cr.mx_quantize_act(xd, rotate=rotate)
+    bc, bsc = cr.mx_quantize_weight(wd, rotate=rotate)
+    y = cr.mx_gemm(ac, asc, bc, bsc)
+    torch.cuda.synchronize()
+    if rotate:
+        oac, oas = oracle.mx_quantize_act_rotated(xb)
+        obc, obs = oracle.mx_quantize_rotated(w)
+    else:
+        oac, oas = oracle.mx_quantize_act(xb)
+        obc, obs = oracle.mx_quantize(w)
+    gu.assert_equal(gu.host(ac), oac, "A codes at k = 2^20")
+    gu.assert_equal(natural_scales(gu.host(asc)), oas, "A scales at k = 2^20")
+    gu.assert_equal(gu.host(bc), obc, "B codes at k = 2^20")
+    gu.assert_equal(natural_scales(gu.host(bsc)), obs, "B scales at k = 2^20")
+    ref, absacc = oracle.mx_gemm(oac, oas, obc, obs)
+    assert_mx_product(gu.host_bf16(y), ref, absacc, k, "mx_gemm 3x5x2^20")
