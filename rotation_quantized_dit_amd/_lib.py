@@ -111,6 +111,9 @@ def _dev(t: torch.Tensor, name: str, dtype: torch.dtype, ndim: int) -> None:
         raise TypeError("%s must be a torch.Tensor" % name)
     if not t.is_cuda:
         raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError("%s is on %s, but the library launches on the current device cuda:%d"
+                         % (name, t.device, torch.cuda.current_device()))
     if t.dtype != dtype:
         raise TypeError("%s must be %s (got %s)" % (name, dtype, t.dtype))
     if t.dim() != ndim:
@@ -166,13 +169,21 @@ def swiglu_rotate_quant_act(gu: torch.Tensor, q_h=None, s_h=None):
     return q_h, s_h
 
 
+def _ws_check(workspace) -> None:
+    """A caller's workspace: a contiguous uint8 tensor on the current GPU."""
+    if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.dtype == torch.uint8
+            and workspace.is_contiguous()):
+        raise TypeError("workspace must be a contiguous uint8 GPU tensor")
+    if workspace.device.index != torch.cuda.current_device():
+        raise ValueError("workspace is on %s, but the library launches on the current device cuda:%d"
+                         % (workspace.device, torch.cuda.current_device()))
+
+
 def _workspace(workspace, m, k, like):
     need = max(workspace_bytes(m, k), 16)
     if workspace is None:
         return torch.empty(need, dtype=torch.uint8, device=like.device)
-    if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.dtype == torch.uint8
-            and workspace.is_contiguous()):
-        raise TypeError("workspace must be a contiguous uint8 GPU tensor")
+    _ws_check(workspace)
     return workspace
 
 
@@ -332,6 +343,9 @@ def _rows_view(t: torch.Tensor, name: str) -> int:
         raise TypeError("%s must be a torch.Tensor" % name)
     if not t.is_cuda:
         raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError("%s is on %s, but the library launches on the current device cuda:%d"
+                         % (name, t.device, torch.cuda.current_device()))
     if t.dtype != torch.bfloat16:
         raise TypeError("%s must be bfloat16 (got %s)" % (name, t.dtype))
     if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
@@ -356,9 +370,7 @@ def _attn_workspace(workspace, s, heads, like):
     need, _ = attention_workspace(s, heads)
     if workspace is None:
         return torch.empty(max(need, 16), dtype=torch.uint8, device=like.device)
-    if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.dtype == torch.uint8
-            and workspace.is_contiguous()):
-        raise TypeError("workspace must be a contiguous uint8 GPU tensor")
+    _ws_check(workspace)
     return workspace
 
 
@@ -375,9 +387,7 @@ def attention_prep(q, k, v, heads: int, workspace=None):
 
 def attention_prepared(workspace, s: int, heads: int, out=None):
     """Attention over a prepared workspace -> bf16 [s, heads * 128]."""
-    if not (isinstance(workspace, torch.Tensor) and workspace.is_cuda and workspace.dtype == torch.uint8
-            and workspace.is_contiguous()):
-        raise TypeError("workspace must be a contiguous uint8 GPU tensor")
+    _ws_check(workspace)
     o = _out(out, (s, heads * ATTN_HEAD_DIM), torch.bfloat16, workspace, "out")
     _check("convrot_attention_prepared", load_library().convrot_attention_prepared(
         workspace.data_ptr(), workspace.numel(), s, heads, ATTN_HEAD_DIM, o.data_ptr(),
