@@ -471,6 +471,38 @@ def main():
             e["pct_int8_peak"] = round(100.0 * o / (d * 1e-3) / 1e12 / PEAK_INT8_TOPS, 1)
         kern[name] = e
 
+    # The vendor library on the same int8 codes, for context: hipBLASLt through
+    # torch._int_mm (int32 output, no scales, no epilogue), each GEMM launched
+    # back to back after the same warmup, next to this library's GEMM timed the
+    # same way.  (The first launches on a cool chip run faster than the steady
+    # state that the power limit settles to, so both sides are warmed up.)
+    def per_launch(fn, reps):
+        for _ in range(args.warmup):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+        ev[0].record()
+        for r in range(reps):
+            fn()
+            ev[r + 1].record()
+        torch.cuda.synchronize()
+        return float(np.median([ev[r].elapsed_time(ev[r + 1]) for r in range(reps)]))
+    vendor = {"library": "hipBLASLt via torch._int_mm (int32 out)"}
+    try:
+        for label, qa, qb, sa, sb, ours, o in (
+                ("gemm_up", qx1, qwu, sx1, swu, lambda: cr.gemm_swiglu(qx1, sx1, qwu, swu, out=h), ops_up),
+                ("gemm_down", qx2, qwd, sx2, swd, lambda: cr.gemm_dequant(qx2, sx2, qwd, swd, out=y), ops_dn)):
+            c32 = torch.empty((qa.shape[0], qb.shape[0]), dtype=torch.int32, device=dev)
+            bt = qb.t()
+            v_ms = per_launch(lambda: torch._int_mm(qa, bt, out=c32), max(args.steps, 5))
+            o_ms = per_launch(ours, max(args.steps, 5))
+            vendor[label] = {"vendor_ms": round(v_ms, 4), "vendor_TOPS": round(o / (v_ms * 1e-3) / 1e12, 1),
+                             "ours_ms": round(o_ms, 4), "ours_TOPS": round(o / (o_ms * 1e-3) / 1e12, 1),
+                             "speedup": round(v_ms / o_ms, 3)}
+            del c32
+    except Exception as exc:   # context only: a library failure does not void the run
+        vendor["error"] = str(exc)[:200]
+    torch.cuda.synchronize()
+
     # The same FFN with SwiGLU on fc1's output side: fc1 writes bf16 gate/up
     # [M, 2I] (dequant epilogue), one pass forms h and rotates + quantizes it,
     # then the same down GEMM.  Same inputs, weights and outputs sizes.
@@ -595,6 +627,7 @@ def main():
         "output_side_swiglu": out_side,
         "weight_quant": {"ms": round(wq_ms, 4), "GB/s": round(wq_bytes / (wq_ms * 1e-3) / 1e9, 1)},
         "device_copy": device_copy,
+        "vendor_int8_gemm": vendor,
         "lora_merge_ffn_up": {"ms": round(merge_ms, 4), "rank": lr,
                               "GB/s": round(merge_bytes / (merge_ms * 1e-3) / 1e9, 1),
                               "note": "dequantize + rank-32 delta + requantize of the 28672 x 5376 weight, "

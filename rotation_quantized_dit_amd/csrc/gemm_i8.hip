@@ -311,18 +311,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                 acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], acc[a][b], 0, 0, 0);
     };
 
-    // Software pipeline.  All STAGES slots are filled up front.  In stage kt:
-    //   k-step 0: MFMAs on registers set 0, interleaved with the reads of
-    //             k-step 1 into set 1;
+    // Software pipeline.  All STAGES slots are filled up front.  Each stage
+    // holds two 32-byte k-steps; in stage kt:
+    //   k-step 0: MFMAs interleaved with the fragment reads of k-step 1;
     //   barrier:  stage kt + 1 has landed (vmcnt) and every wave has read both
     //             k-steps of stage kt (lgkmcnt before the barrier);
-    //   k-step 1: MFMAs on set 1, interleaved with the refill of stage kt's
-    //             slot with stage kt + STAGES and the reads of stage kt + 1's
-    //             k-step 0 into set 0.
+    //   k-step 1: MFMAs interleaved with the refill of stage kt's slot with
+    //             stage kt + STAGES and the reads of stage kt + 1's k-step 0.
     // At stage kt's barrier the stages after kt + 1 may stay in flight
-    // (STAGES - 2 of them, COPIES copies each).  The steady-state loop runs
-    // while a refill remains; the last stages are peeled so that the loop
-    // body is straight-line code.
+    // (STAGES - 2 of them, COPIES copies each).  With 384-row tiles the reads
+    // refill the registers of the fragments the MFMAs have finished with;
+    // the 256-row variant has room for two fragment sets, runs a steady-state
+    // loop while a refill remains and peels the last stages.
     constexpr int NREAD = MA + 4;        // fragment reads per k-step
     constexpr int NMFMA = 4 * MA;        // MFMAs per k-step
     const int KT = K / BK;
@@ -345,28 +345,53 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     int kt = 0;
     int slot = 0;                        // slot of stage kt
     if constexpr (MA == 3) {
-        // 192 accumulators leave room for one fragment set only: each k-step
-        // reads its fragments and then issues its MFMAs (the other wave of the
-        // SIMD fills the read latency); the barrier sits between the k-steps,
-        // after the last reads of stage kt, and the refill of its slot is
-        // interleaved with the second k-step's MFMAs.
+        // 192 accumulators leave room for one fragment set only.  Each k-step
+        // issues its MFMAs row by row (A block 0 with B blocks 0-3, then A
+        // block 1, then A block 2), and every fragment register is refilled
+        // with the next k-step's fragment as soon as the last MFMA that reads
+        // it has issued: A blocks 0 and 1 after their rows, the B blocks and
+        // A block 2 during the last row.  The reads of one k-step thus run
+        // under the MFMAs of the one before, with no second register set.
+        // (Reading all seven fragments first and then issuing the MFMAs left
+        // the matrix core idle at every k-step for the read latency whenever
+        // the two waves of a SIMD reached their reads together, as they do
+        // after each barrier; measured 4-5 % slower on both FFN GEMMs.)
         v4i fa[MA], fb[4];
+        auto mma_refill = [&](const int8_t* st, int s) {
+#pragma unroll
+            for (int a = 0; a < MA - 1; ++a) {
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[a], fb[b], acc[a][b], 0, 0, 0);
+                fa[a] = *reinterpret_cast<const v4i*>(st + a_off[s][a]);
+            }
+#pragma unroll
+            for (int b = 0; b < 4; ++b) {
+                acc[MA - 1][b] =
+                    __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[MA - 1], fb[b], acc[MA - 1][b], 0, 0, 0);
+                fb[b] = *reinterpret_cast<const v4i*>(st + b_off[s][b]);
+            }
+            fa[MA - 1] = *reinterpret_cast<const v4i*>(st + a_off[s][MA - 1]);
+        };
+        read_frags(lds, 0, fa, fb);
         for (; kt < KT; ++kt) {
             const int next = slot + 1 == STAGES ? 0 : slot + 1;
             const bool refill = kt + STAGES < KT;
             __builtin_amdgcn_sched_barrier(0);
-            read_frags(lds + slot * STAGE_BYTES, 0, fa, fb);
-            mma(fa, fb);
+            // k-step 0 of stage kt, reading k-step 1 of the same slot
+            mma_refill(lds + slot * STAGE_BYTES, 1);
             __builtin_amdgcn_sched_barrier(0);
-            read_frags(lds + slot * STAGE_BYTES, 1, fa, fb);
-            // stage kt + 1 must have landed before the next iteration reads it
+            // stage kt + 1 must have landed before its fragments are read
             const int after = KT - 2 - kt;   // stages behind kt + 1 in flight (<= STAGES - 2)
             if (after >= 1) wait_vmcnt<COPIES>();
             else wait_vmcnt<0>();
             lds_barrier();
             __builtin_amdgcn_sched_barrier(0);
             if (refill) issue(kt + STAGES, slot);
-            mma(fa, fb);
+            __builtin_amdgcn_sched_barrier(0);
+            // k-step 1 of stage kt, reading k-step 0 of stage kt + 1 (after
+            // the last stage this reads a landed slot whose values go unused)
+            mma_refill(lds + next * STAGE_BYTES, 0);
             __builtin_amdgcn_sched_barrier(0);
             slot = next;
         }
