@@ -227,7 +227,8 @@ int convrot_merge_lora(const int8_t* q_w, const float* s_w, int64_t n, int64_t k
  * evaluation of the same definition to the rounding of the fp16 probabilities,
  * the fp32 sums and the bf16 store.
  *
- * Shapes: 0 <= s <= 2^24, heads >= 0, head_dim == 128; ld and ld_out are
+ * Shapes: 0 <= s <= 2^24 - 64 (one head's fp16 V blocks must fit a 32-bit
+ * byte range), heads >= 0, head_dim == 128; ld and ld_out are
  * multiples of 8 and at least heads * 128.  s == 0 or heads == 0 is success
  * with nothing enqueued.  V values beyond the fp16 range give unspecified
  * outputs.  The output must not overlap the inputs or the workspace.

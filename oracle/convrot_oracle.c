@@ -14,10 +14,10 @@
  * (each row's arithmetic is identical whatever the thread count).
  *
  * Sources of what is computed (the pages):
- *   - cloud-worker docs/RESEARCH.md, "Weight families": int8_convrot is
- *     rotation-based post-training quantization; a group-wise Hadamard rotation,
- *     written as a convolution, spreads activation outliers so that int8
- *     quantization is close to lossless.
+ *   - cloud-worker docs/RESEARCH.md, "Weight families": the int8_convrot
+ *     weight family; what this file computes for it is a block-diagonal
+ *     orthonormal Hadamard-256 transform along K, applied before per-row
+ *     symmetric int8 quantization of both operands.
  *   - h3-rs README, model file table: the DiT weights are "int8 per-row +
  *     ConvRot (Hadamard-256)", i.e. one scale per output row, Hadamard groups of
  *     256 along the contraction dimension.

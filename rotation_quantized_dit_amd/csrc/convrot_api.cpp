@@ -232,7 +232,9 @@ int convrot_linear_swiglu(const uint16_t* x, int64_t m, int64_t k, const int8_t*
 
 namespace {
 
-constexpr int64_t kAttnMaxS = (int64_t)1 << 24;
+// The flash kernel addresses one head's V^T blocks (s_pad x 128 fp16) through a
+// 32-bit buffer range, so s_pad * 256 must stay below 2^32: s_pad <= 2^24 - 64.
+constexpr int64_t kAttnMaxS = ((int64_t)1 << 24) - 64;
 
 inline size_t align256(size_t x) { return (x + 255u) & ~(size_t)255u; }
 

@@ -14,41 +14,58 @@
 //            evaluated with the hardware base-2 exponential and reciprocal
 //            (see swiglu_hw).
 //
-// Tiling.  A workgroup of 8 waves (two per SIMD) owns a BM x 256 tile of acc
-// (BM tokens; for SwiGLU 128 gate columns + the matching 128 up columns).
-// Waves form a 4 (rows) x 2 (columns) grid; each owns 32 MA x 128 (MA =
-// BM / 128) as MA x 4 blocks of v_mfma_i32_32x32x32_i8 (32 x 32 outputs,
-// 32 bytes of K per instruction, 16 int32 accumulators per lane per block).
-// For SwiGLU a wave's 128 columns are 64 gate columns and the 64 up columns of
-// the same outputs, so every lane holds g and u of its elements.  K advances
-// 64 bytes per stage through an LDS ring of STAGES slots.
-//
-// Why two waves per SIMD: each SIMD issues at most one instruction per wave
-// every few cycles, and the fragment reads, the ring refills and their
-// address set-up of one wave would otherwise sit in the gaps of that same
-// wave's MFMA stream; with a second wave on the SIMD the matrix core takes
-// MFMAs from whichever wave has one ready.
+// Tiling.  A workgroup of 8 waves (two per SIMD) owns a 384 x 256 tile of acc
+// (384 tokens; for SwiGLU 128 gate columns + the matching 128 up columns).
+// Waves form a 4 (rows) x 2 (columns) grid; each owns 96 x 128 as 3 x 4 blocks
+// of v_mfma_i32_32x32x32_i8 (32 x 32 outputs, 32 bytes of K per instruction,
+// 16 int32 accumulators per lane per block, 192 in all).  For SwiGLU a wave's
+// 128 columns are 64 gate columns and the 64 up columns of the same outputs,
+// so every lane holds g and u of its elements.  Two waves per SIMD let the
+// matrix core take MFMAs from whichever wave has one ready while the other
+// waits on a fragment read, a copy or the stage barrier.
 //
 // Operand streaming.  Both operands are K-contiguous rows (q_x is [M, K] and
 // q_w is [N, K]), which is the MFMA operand layout: a lane takes 16
-// contiguous bytes of one row.  Global -> LDS copies use the direct buffer
-// load (buffer_load_dwordx4 ... lds: 64 lanes x 16 B land contiguously in
-// LDS, no VGPR staging); the per-lane row offset is a fixed register, the
-// K position a scalar offset, so one copy costs one M0 move and one load.
-// Each LDS row is 64 bytes (4 chunks of 16 B); chunk c of row r is stored at
-// position c ^ ((r >> 2) & 3), which makes the 16-byte fragment reads of 16
-// consecutive rows hit distinct banks.  The XOR is applied on the global
-// side, so the copies stay contiguous in LDS.
+// contiguous bytes of one row.  K advances 64 bytes per stage through a ring
+// of 4 LDS slots (40 KiB each, the whole 160 KiB).  Global -> LDS copies are
+// direct buffer loads (buffer_load_dwordx4 ... lds: 64 lanes x 16 B land
+// contiguously in LDS, no VGPR staging): each wave copies 48 rows of A and 32
+// rows of B per stage, five copies.  Each LDS row is 64 bytes (4 chunks of
+// 16 B); chunk c of row r is stored at position c ^ ((r >> 2) & 3), so the
+// 16-byte fragment reads of 16 consecutive rows hit distinct banks; the XOR
+// is applied on the global side, so the copies stay contiguous in LDS.
+//
+// The copies are issued from inline assembly.  The compiler's wait-count pass
+// treats any LDS read that follows an LDS-writing buffer load it cannot prove
+// disjoint as dependent on it, and drains every outstanding copy (vmcnt(0))
+// before the fragment reads of each stage, which removes the prefetch.  Here
+// the ring discipline (explicit vmcnt waits and the stage barrier) orders
+// copies and reads, so the copies are hidden from that pass; M0, which holds
+// the LDS destination, is passed as an input operand, so the compiler knows
+// it is set.
+//
+// Main loop (one stage = two k-steps of 12 MFMAs per wave), one basic block:
+//   - the MFMAs run in a fixed order (A0 x B0..B3, then A1/A2 alternating
+//     over B0..B3), and each fragment register is refilled with the next
+//     k-step's fragment right after its last use, which spreads the seven
+//     reads over the k-step and gives each at least four MFMAs of latency;
+//   - the stage barrier sits after the fourth MFMA of the second k-step, so
+//     each wave enters it with MFMAs in flight; before it, a vmcnt wait
+//     makes this wave's copies of the next stage complete, and lgkmcnt(0)
+//     makes its reads of the current slot complete;
+//   - after the barrier the current slot is refilled with the stage four
+//     ahead: three copies spread over the rest of that k-step, the last two
+//     in the next stage's first k-step.
+// Past the last stage the copies are still issued (so every iteration is the
+// same basic block and the vmcnt counts stay uniform) but with the voffset
+// pushed beyond the buffer's range: the hardware returns zeros without a
+// memory access and they land in slots no one reads again.
 //
 // Scheduling.  Workgroups are dealt round-robin to the 8 XCDs; the tile id is
 // remapped so that each XCD walks a contiguous range of tiles in a grouped
-// raster (GROUP_M M-tiles per group, N fastest within a group), so workgroups
-// that run together on one XCD share A and B panels in that XCD's L2.  With 2
-// M-tiles per group the 32 tiles an XCD runs at once span 2 A panels and 16 B
-// panels: each A panel is fetched from HBM about once, and the weight panels,
-// re-read once per group, stay in the 256 MB Infinity Cache.  (8 M-tiles per
-// group re-read A panels four times as often, beyond what the cache holds for
-// the 462 MB activation of the down projection; 2 measured 4-5 % faster there.)
+// raster (2 M-tiles per group, N fastest within a group), so workgroups that
+// run together on one XCD share A and B panels in that XCD's L2, and the
+// weight panels, re-read once per group, stay in the 256 MB Infinity Cache.
 //
 // Ragged edges: rows past M or N are clamped to the last row for loading and
 // masked at the store.
@@ -61,44 +78,37 @@
 namespace convrot {
 namespace {
 
-#ifndef CONVROT_GEMM_BM
-#define CONVROT_GEMM_BM 384
-#endif
-constexpr int BM = CONVROT_GEMM_BM;   // tile rows (tokens): 4 wave rows x 32 MA
+constexpr int BM = 384;               // tile rows (tokens): 4 wave rows x 96
 constexpr int BN = 256;               // tile columns (weight rows)
-constexpr int BK = 64;
-constexpr int MA = BM / 128;          // 32-row A blocks per wave
+constexpr int BK = 64;                // K bytes per stage
+constexpr int MA = 3;                 // 32-row A blocks per wave
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int A_STAGE = BM * BK;
 constexpr int B_STAGE = BN * BK;
 constexpr int STAGE_BYTES = A_STAGE + B_STAGE;
+constexpr int STAGES = 4;
+constexpr int RING_BYTES = STAGES * STAGE_BYTES;
 // copies per wave per stage: MA of A (16 rows each) and 2 of B
 constexpr int COPIES = MA + 2;
+// copies of a refill issued in the k-step after the stage barrier; the rest
+// go out in the next stage's first k-step
+constexpr int COPIES_NOW = 3;
 // Epilogue staging: each wave parks 32 rows x 128 int32 at a time, rows
-// padded to PITCH int32 to spread banks; it reuses the ring's memory.
+// padded to PITCH int32 to spread banks; it reuses the ring's memory, and
+// the tile's row scales follow it.
 constexpr int PITCH = 136;
 constexpr int STASH_WAVE_BYTES = 32 * PITCH * 4;
 constexpr int STASH_BYTES = NWAVES * STASH_WAVE_BYTES;
-// as many ring stages (at most 4) as fit in 160 KiB of LDS with the stash
-// (which reuses the ring) and the tile's row scales
-constexpr int lds_for(int stages) {
-    return (stages * STAGE_BYTES > STASH_BYTES ? stages * STAGE_BYTES : STASH_BYTES) + 4 * BM;
-}
-constexpr int STAGES = lds_for(4) <= 160 * 1024 ? 4 : 3;
-constexpr int RING_BYTES = STAGES * STAGE_BYTES;
-constexpr int LDS_BYTES = RING_BYTES > STASH_BYTES ? RING_BYTES : STASH_BYTES;
-#ifndef CONVROT_GEMM_GROUP_M
-#define CONVROT_GEMM_GROUP_M 2
-#endif
-constexpr int GROUP_M = CONVROT_GEMM_GROUP_M;   // M-tiles per raster group
-static_assert(BM % 128 == 0 && MA >= 2 && MA <= 3, "tile rows");
-static_assert(LDS_BYTES + 4 * BM <= 160 * 1024, "LDS budget");
+constexpr int SX_OFFSET = STASH_BYTES;
+constexpr int GROUP_M = 2;            // M-tiles per raster group
+static_assert(RING_BYTES <= 160 * 1024, "LDS budget");
+static_assert(SX_OFFSET + 4 * BM <= RING_BYTES, "row scales after the stash, inside the ring");
+static_assert(STAGES * COPIES < 64, "vmcnt range");
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
@@ -110,34 +120,43 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
 }
 
-// Workgroup barrier for the LDS ring.  Completion of the direct copies is
-// established by the explicit vmcnt wait that precedes it, and the fragment
-// reads of the previous stage by an lgkmcnt(0) wait; so only the hardware
-// barrier is needed, plus a compiler barrier that keeps LDS accesses on their
-// side of it.  (A fenced __syncthreads() would drain every outstanding
-// prefetch with vmcnt(0).)
+// lgkmcnt(0): every LDS read of this wave has returned.
+__device__ __forceinline__ void wait_lds_reads() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Workgroup barrier for the LDS ring: this wave's fragment reads are complete
+// (lgkmcnt(0)) before any wave can pass it and refill the slot they read.
+// Completion of the copies is established by the explicit vmcnt wait before
+// it.  (A fenced __syncthreads() would drain every outstanding copy.)
 __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
-    // lgkmcnt(0): this wave's fragment reads are complete before any wave can
-    // pass the barrier and refill the slot they read.
-    __builtin_amdgcn_s_waitcnt(0xC07F);
+    wait_lds_reads();
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
 }
 
-// One direct copy: 64 lanes x 16 bytes from rsrc + voff + soff into LDS at
-// dst + 16 * lane.
-__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t rsrc, int8_t* dst, uint32_t voff,
-                                       uint32_t soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voff, soff, 0, 0);
-#endif
+// Buffer resource words over [base, base + bytes) (raw, no stride; gfx9
+// dword 3), uniform across the wave.
+__device__ __forceinline__ v4u rsrc_words(const int8_t* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    v4u r;
+    r.x = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    r.y = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    r.z = __builtin_amdgcn_readfirstlane(bytes);
+    r.w = 0x00020000u;
+    return r;
 }
 
-// Buffer resource over [base, base + bytes) (raw, no stride; gfx9 dword 3).
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const int8_t* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
+// One direct copy: 64 lanes x 16 bytes from rsrc + voff + soff into LDS at
+// lds_addr + 16 * lane.  The load writes no VGPR; its address operands are
+// read at issue.
+__device__ __forceinline__ void copy16(v4u rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr));
 }
+
+// Past-the-end offset for copies of stages beyond the last: beyond any
+// buffer's num_records (< 2^31), so the load returns zeros and touches no memory.
+constexpr uint32_t OOB = 0x80000000u;
 
 __device__ __forceinline__ float dequant(int acc, float sx, float sw) {
     float f = (float)acc;
@@ -182,33 +201,30 @@ template <Epilogue EP>
 __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     const int8_t* __restrict__ A, const float* __restrict__ sx, const int8_t* __restrict__ B,
     const float* __restrict__ sw, int M, int N, int K, void* __restrict__ out, int MT, int NT) {
-    __shared__ __attribute__((aligned(1024))) int8_t lds[LDS_BYTES];
-    __shared__ float sx_lds[BM];
+    __shared__ __attribute__((aligned(1024))) int8_t lds[RING_BYTES];
 
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int wm = wave >> 1;   // band of 32 MA rows of the tile
+    const int wm = wave >> 1;   // band of 96 rows of the tile
     const int wn = wave & 1;    // column half of the tile
     const Tile tile = map_tile(blockIdx.x, MT, NT);
     const int m0 = tile.tm * BM;
     const int rows_a = (M - m0) < BM ? (M - m0) : BM;
 
     // Epilogue scales, loaded before the main loop so that their latency is
-    // hidden: s_x of the tile's rows into LDS (read back per output row), and
-    // s_w of the lane's 8 output columns (gate and up columns for SwiGLU) into
-    // registers.  (Keeping these register loads outstanding across the main
-    // loop also keeps the compiler from draining the ring's copies before the
-    // first fragment read of every stage, as it does when no other vector
-    // load is pending there.)
+    // hidden: s_x of the tile's row tid into a register (parked in LDS after
+    // the loop, where the ring was), and s_w of the lane's 8 output columns
+    // (gate and up columns for SwiGLU).
     constexpr int EPI_CG = EP == Epilogue::SWIGLU ? 8 : 16;   // column groups per wave row
     const int epi_cg = lane % EPI_CG;
     const int epi_ro = lane / EPI_CG;
     const int epi_col0 = EP == Epilogue::SWIGLU ? tile.tn * (BN / 2) + 64 * wn + 8 * epi_cg
                                                 : tile.tn * BN + 128 * wn + 8 * epi_cg;
+    float sx_own = 0.0f;
     float swa[8], swb[8];
     if constexpr (EP != Epilogue::S32) {
-        if (tid < BM) sx_lds[tid] = sx[tid < rows_a ? m0 + tid : M - 1];
+        if (tid < BM) sx_own = sx[tid < rows_a ? m0 + tid : M - 1];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const int c = (epi_col0 + e) < N ? (epi_col0 + e) : (N - 1);
@@ -229,14 +245,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         b_first = tile.tn * BN;
     const int b_span = EP == Epilogue::SWIGLU ? BN / 2 : BN;
     const int rows_b = (N - b_first) < b_span ? (N - b_first) : b_span;
-    const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(A + (int64_t)m0 * K, (uint32_t)rows_a * (uint32_t)K);
-    __amdgpu_buffer_rsrc_t rsrc_b;
+    const v4u rsrc_a = rsrc_words(A + (int64_t)m0 * K, (uint32_t)rows_a * (uint32_t)K);
+    v4u rsrc_b;
     if constexpr (EP == Epilogue::SWIGLU) {
         // waves 0-3 copy B rows 0-127 (gate), waves 4-7 rows 128-255 (up)
         const int64_t first = wave < 4 ? b_first : (int64_t)N + b_first;
-        rsrc_b = make_rsrc(B + first * K, (uint32_t)rows_b * (uint32_t)K);
+        rsrc_b = rsrc_words(B + first * K, (uint32_t)rows_b * (uint32_t)K);
     } else {
-        rsrc_b = make_rsrc(B + (int64_t)b_first * K, (uint32_t)rows_b * (uint32_t)K);
+        rsrc_b = rsrc_words(B + (int64_t)b_first * K, (uint32_t)rows_b * (uint32_t)K);
     }
     uint32_t voff[COPIES];
 #pragma unroll
@@ -255,14 +271,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         }
         voff[i] = (uint32_t)src_row * (uint32_t)K + 16u * (uint32_t)c;
     }
-    auto issue = [&](int kt, int slot) {
-        int8_t* a_dst = lds + slot * STAGE_BYTES + 16 * 64 * MA * wave;
-        int8_t* b_dst = lds + slot * STAGE_BYTES + A_STAGE + 32 * 64 * wave;
-        const uint32_t soff = (uint32_t)kt * BK;
-#pragma unroll
-        for (int i = 0; i < MA; ++i) copy16(rsrc_a, a_dst + 1024 * i, voff[i], soff);
-        copy16(rsrc_b, b_dst, voff[MA], soff);
-        copy16(rsrc_b, b_dst + 1024, voff[MA + 1], soff);
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int8_t*)lds);
+    // copy i of the stage at K byte soff into ring slot `slot` (oob: 0 or OOB)
+    auto issue = [&](int i, uint32_t soff, uint32_t oob, int slot) {
+        const uint32_t dst = i < MA ? lds_base + slot * STAGE_BYTES + 1024 * (MA * wave + i)
+                                    : lds_base + slot * STAGE_BYTES + A_STAGE + 2048 * wave + 1024 * (i - MA);
+        copy16(i < MA ? rsrc_a : rsrc_b, dst, voff[i] + oob, soff);
     };
 
     // LDS rows of this lane's fragments: A blocks a < MA (rows of the wave's
@@ -277,15 +292,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         else
             b_row[b] = 128 * wn + 32 * b + (lane & 31);
     }
-
-    v16i acc[MA][4];
-#pragma unroll
-    for (int a = 0; a < MA; ++a)
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
-
     // Byte offsets (within a stage) of this lane's 16-byte fragment reads for
     // the two 32-byte k-steps of a stage.
     int a_off[2][MA], b_off[2][4];
@@ -297,170 +303,133 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
 #pragma unroll
         for (int b = 0; b < 4; ++b) b_off[s][b] = A_STAGE + b_row[b] * BK + 16 * (c ^ swz(b_row[b]));
     }
-    auto read_frags = [&](const int8_t* st, int s, v4i (&af)[MA], v4i (&bf)[4]) {
-#pragma unroll
-        for (int a = 0; a < MA; ++a) af[a] = *reinterpret_cast<const v4i*>(st + a_off[s][a]);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) bf[b] = *reinterpret_cast<const v4i*>(st + b_off[s][b]);
-    };
-    auto mma = [&](const v4i (&af)[MA], const v4i (&bf)[4]) {
-#pragma unroll
-        for (int a = 0; a < MA; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b)
-                acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(af[a], bf[b], acc[a][b], 0, 0, 0);
-    };
 
-    // Software pipeline.  All STAGES slots are filled up front.  Each stage
-    // holds two 32-byte k-steps; in stage kt:
-    //   k-step 0: MFMAs interleaved with the fragment reads of k-step 1;
-    //   barrier:  stage kt + 1 has landed (vmcnt) and every wave has read both
-    //             k-steps of stage kt (lgkmcnt before the barrier);
-    //   k-step 1: MFMAs interleaved with the refill of stage kt's slot with
-    //             stage kt + STAGES and the reads of stage kt + 1's k-step 0.
-    // At stage kt's barrier the stages after kt + 1 may stay in flight
-    // (STAGES - 2 of them, COPIES copies each).  With 384-row tiles the reads
-    // refill the registers of the fragments the MFMAs have finished with;
-    // the 256-row variant has room for two fragment sets, runs a steady-state
-    // loop while a refill remains and peels the last stages.
-    constexpr int NREAD = MA + 4;        // fragment reads per k-step
-    constexpr int NMFMA = 4 * MA;        // MFMAs per k-step
+    v16i acc[MA][4];
+#pragma unroll
+    for (int a = 0; a < MA; ++a)
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
+
+    // Prologue: fill every slot (stages past the last go out of range), wait
+    // for stage 0, read its first k-step's fragments.
     const int KT = K / BK;
-    // (The conditional issue and the branch on the stages ahead are kept in
-    // this form on purpose: with an unconditional prologue the compiler
-    // inserts a full vmcnt(0) before the first fragment read of every stage
-    // of the main loop, which drains the prefetch.)
 #pragma unroll
     for (int st = 0; st < STAGES; ++st)
-        if (st < KT) issue(st, st);
-    {
-        const int ahead = (KT - 1) < (STAGES - 1) ? (KT - 1) : (STAGES - 1);
-        if (STAGES >= 4 && ahead >= 3) wait_vmcnt<(STAGES >= 4 ? 3 : 2) * COPIES>();
-        else if (ahead >= 2) wait_vmcnt<2 * COPIES>();
-        else if (ahead == 1) wait_vmcnt<COPIES>();
-        else wait_vmcnt<0>();
-    }
+#pragma unroll
+        for (int i = 0; i < COPIES; ++i) issue(i, (uint32_t)st * BK, st < KT ? 0u : OOB, st);
+    wait_vmcnt<(STAGES - 1) * COPIES>();
     lds_barrier();
+    v4i fa[MA], fb[4];
+#pragma unroll
+    for (int a = 0; a < MA; ++a) fa[a] = *reinterpret_cast<const v4i*>(lds + a_off[0][a]);
+#pragma unroll
+    for (int b = 0; b < 4; ++b) fb[b] = *reinterpret_cast<const v4i*>(lds + b_off[0][b]);
+    // nothing of the prologue (scalar loads included) stays pending in
+    // lgkmcnt, so the loop's waits on its fragment reads can be exact
+    wait_lds_reads();
+    __builtin_amdgcn_sched_barrier(0);
 
-    int kt = 0;
-    int slot = 0;                        // slot of stage kt
-    if constexpr (MA == 3) {
-        // 192 accumulators leave room for one fragment set only.  Each k-step
-        // issues its MFMAs row by row (A block 0 with B blocks 0-3, then A
-        // block 1, then A block 2), and every fragment register is refilled
-        // with the next k-step's fragment as soon as the last MFMA that reads
-        // it has issued: A blocks 0 and 1 after their rows, the B blocks and
-        // A block 2 during the last row.  The reads of one k-step thus run
-        // under the MFMAs of the one before, with no second register set.
-        // (Reading all seven fragments first and then issuing the MFMAs left
-        // the matrix core idle at every k-step for the read latency whenever
-        // the two waves of a SIMD reached their reads together, as they do
-        // after each barrier; measured 4-5 % slower on both FFN GEMMs.)
-        v4i fa[MA], fb[4];
-        auto mma_refill = [&](const int8_t* st, int s) {
-#pragma unroll
-            for (int a = 0; a < MA - 1; ++a) {
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-                    acc[a][b] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[a], fb[b], acc[a][b], 0, 0, 0);
-                fa[a] = *reinterpret_cast<const v4i*>(st + a_off[s][a]);
-            }
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                acc[MA - 1][b] =
-                    __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[MA - 1], fb[b], acc[MA - 1][b], 0, 0, 0);
-                fb[b] = *reinterpret_cast<const v4i*>(st + b_off[s][b]);
-            }
-            fa[MA - 1] = *reinterpret_cast<const v4i*>(st + a_off[s][MA - 1]);
-        };
-        read_frags(lds, 0, fa, fb);
-        for (; kt < KT; ++kt) {
-            const int next = slot + 1 == STAGES ? 0 : slot + 1;
-            const bool refill = kt + STAGES < KT;
-            __builtin_amdgcn_sched_barrier(0);
-            // k-step 0 of stage kt, reading k-step 1 of the same slot
-            mma_refill(lds + slot * STAGE_BYTES, 1);
-            __builtin_amdgcn_sched_barrier(0);
-            // stage kt + 1 must have landed before its fragments are read
-            const int after = KT - 2 - kt;   // stages behind kt + 1 in flight (<= STAGES - 2)
-            if (after >= 1) wait_vmcnt<COPIES>();
-            else wait_vmcnt<0>();
-            lds_barrier();
-            __builtin_amdgcn_sched_barrier(0);
-            if (refill) issue(kt + STAGES, slot);
-            __builtin_amdgcn_sched_barrier(0);
-            // k-step 1 of stage kt, reading k-step 0 of stage kt + 1 (after
-            // the last stage this reads a landed slot whose values go unused)
-            mma_refill(lds + next * STAGE_BYTES, 0);
-            __builtin_amdgcn_sched_barrier(0);
-            slot = next;
+    // The fixed MFMA order of a k-step (slot i: A block SA[i] x B block SB[i])
+    // and the refill points: A0 after slot 3, B0 after 5, B1 after 7, B2
+    // after 9, B3, A1 and A2 after 11.
+    constexpr int SA[12] = {0, 0, 0, 0, 1, 2, 1, 2, 1, 2, 1, 2};
+    constexpr int SB[12] = {0, 1, 2, 3, 0, 0, 1, 1, 2, 2, 3, 3};
+    auto mfma = [&](int i) {
+        acc[SA[i]][SB[i]] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[SA[i]], fb[SB[i]], acc[SA[i]][SB[i]], 0, 0, 0);
+    };
+    auto refill = [&](int i, const int8_t* st, int s) {
+        if (i == 3) fa[0] = *reinterpret_cast<const v4i*>(st + a_off[s][0]);
+        if (i == 5) fb[0] = *reinterpret_cast<const v4i*>(st + b_off[s][0]);
+        if (i == 7) fb[1] = *reinterpret_cast<const v4i*>(st + b_off[s][1]);
+        if (i == 9) fb[2] = *reinterpret_cast<const v4i*>(st + b_off[s][2]);
+        if (i == 11) {
+            fb[3] = *reinterpret_cast<const v4i*>(st + b_off[s][3]);
+            fa[1] = *reinterpret_cast<const v4i*>(st + a_off[s][1]);
+            fa[2] = *reinterpret_cast<const v4i*>(st + a_off[s][2]);
         }
-    } else {
-    v4i fa0[MA], fb0[4], fa1[MA], fb1[4];
-    read_frags(lds, 0, fa0, fb0);
-    for (; kt + STAGES < KT; ++kt) {
+    };
+    // copy j (< COPIES_NOW) of a refill goes out after slot CS[j] of the
+    // k-step that follows the barrier; copies COPIES_NOW.. after slots 0 and 6
+    // of the next stage's first k-step
+    constexpr int CS[COPIES_NOW] = {4, 7, 10};
+    constexpr int BARRIER_AFTER = 3;
+
+    int slot = 0;
+    uint32_t soff = (uint32_t)STAGES * BK;
+    // Before the first refill, the deferred copies of stage STAGES - 1 are
+    // issued once more (the same bytes into a slot no one reads before they
+    // land), so that every iteration has the same shape.
+    int prev_slot = STAGES - 1;
+    uint32_t prev_soff = (uint32_t)(STAGES - 1) * BK, prev_oob = 0;
+    for (int kt = 0; kt < KT; ++kt) {
         const int next = slot + 1 == STAGES ? 0 : slot + 1;
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1);
-        mma(fa0, fb0);
+        const uint32_t oob = kt + STAGES < KT ? 0u : OOB;
+        const int8_t* cur = lds + slot * STAGE_BYTES;
+        const int8_t* nxt = lds + next * STAGE_BYTES;
+        // k-step 0 of stage kt; refills from k-step 1 of the same slot
 #pragma unroll
-        for (int i = 0; i < NREAD; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(i);
+            refill(i, cur, 1);
+            if (i == 0) issue(COPIES_NOW, prev_soff, prev_oob, prev_slot);
+            if (i == 6) issue(COPIES_NOW + 1, prev_soff, prev_oob, prev_slot);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
+        // k-step 1: the first slots run on fragments already in registers
+#pragma unroll
+        for (int i = 0; i <= BARRIER_AFTER; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(i);
+        }
         __builtin_amdgcn_sched_barrier(0);
+        // Stage kt + 1 has landed: this wave's copies of it (only the two
+        // later stages' copies may still be in flight), then every wave's.
         wait_vmcnt<(STAGES - 2) * COPIES>();
         lds_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(lds + next * STAGE_BYTES, 0, fa0, fb0);
-        issue(kt + STAGES, slot);
-        mma(fa1, fb1);
 #pragma unroll
-        for (int i = 0; i < COPIES; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // one direct copy
-        }
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (i > BARRIER_AFTER) mfma(i);
+            if (i == BARRIER_AFTER) {
 #pragma unroll
-        for (int i = COPIES; i < NREAD; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // one LDS read
+                for (int j = 0; j <= BARRIER_AFTER; ++j) refill(j, nxt, 0);
+            } else if (i > BARRIER_AFTER) {
+                refill(i, nxt, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < COPIES_NOW; ++j)
+                if (CS[j] == i) issue(j, soff, oob, slot);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, NMFMA - NREAD, 0);
         __builtin_amdgcn_sched_barrier(0);
+        prev_slot = slot;
+        prev_soff = soff;
+        prev_oob = oob;
         slot = next;
+        soff += BK;
     }
-    // Peeled tail: the stages with a successor, then the last.
-    for (; kt + 1 < KT; ++kt) {
-        const int next = slot + 1 == STAGES ? 0 : slot + 1;
-        read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1);
-        mma(fa0, fb0);
-        const int after = KT - 2 - kt;   // stages behind kt + 1 still in flight (<= STAGES - 2)
-        if (STAGES >= 4 && after >= 2) wait_vmcnt<2 * COPIES>();
-        else if (after >= 1) wait_vmcnt<COPIES>();
-        else wait_vmcnt<0>();
-        lds_barrier();
-        read_frags(lds + next * STAGE_BYTES, 0, fa0, fb0);
-        mma(fa1, fb1);
-        slot = next;
-    }
-    read_frags(lds + slot * STAGE_BYTES, 1, fa1, fb1);
-    mma(fa0, fb0);
-    mma(fa1, fb1);
-    }
+    // the deferred copies of the last refill (out of range), then no copy may
+    // still be writing the ring, which the epilogue reuses
+#pragma unroll
+    for (int i = COPIES_NOW; i < COPIES; ++i) issue(i, prev_soff, OOB, prev_slot);
+    wait_vmcnt<0>();
 
     // Epilogue.  Block (a, b), lane l, register r of the MFMA accumulators
     // holds row 32 a + 8 (r / 4) + 4 (l / 32) + r % 4 and column 32 b + l % 32
-    // of the wave's 32 MA x 128 sub-tile.  Row block by row block, each wave
+    // of the wave's 96 x 128 sub-tile.  Row block by row block, each wave
     // parks its 32 x 128 int32 accumulators in its own part of the (now free)
     // ring, then reads them back row-contiguous: every lane takes 8
     // consecutive columns of one row, applies the scales and the epilogue math
     // in a compact loop, and writes one 16-byte store.
     lds_barrier();   // every wave is done reading the ring
+    float* sx_lds = reinterpret_cast<float*>(lds + SX_OFFSET);
+    if constexpr (EP != Epilogue::S32) {
+        if (tid < BM) sx_lds[tid] = sx_own;
+        lds_barrier();
+    }
     int32_t* stash = reinterpret_cast<int32_t*>(lds + wave * STASH_WAVE_BYTES);
     const int grow0 = m0 + 32 * MA * wm;
-
 
     auto stash_block = [&](int a) {
         asm volatile("" ::: "memory");

@@ -199,6 +199,14 @@ def test_attention_validation(L):
     assert L.convrot_attention_workspace(65, 2, 64, None) == 0
     assert L.convrot_attention_workspace(-1, 2, 128, None) == 0
     assert L.convrot_attention_workspace((1 << 24) + 1, 1, 128, None) == 0
+    # the largest accepted s: one head's V blocks (s_pad x 128 fp16) end just
+    # below 2^32 bytes; every s that pads to 2^24 keys is rejected before launch
+    assert L.convrot_attention_workspace((1 << 24) - 64, 1, 128, None) > 0
+    for s in ((1 << 24) - 63, (1 << 24) - 1, 1 << 24):
+        assert L.convrot_attention_workspace(s, 1, 128, None) == 0, s
+        assert L.convrot_attention_prep(A, B, C, 128, s, 1, 128, D, 1 << 40, None) == ERR_SHAPE, s
+        assert L.convrot_attention_prepared(D, 1 << 40, s, 1, 128, A, 128, None) == ERR_SHAPE, s
+        assert L.convrot_attention(A, B, C, 128, s, 1, 128, A, 128, D, 1 << 40, None) == ERR_SHAPE, s
     assert L.convrot_attention_workspace(0, 5, 128, None) == 0
     ld = 3 * 2 * 128
     assert L.convrot_attention_prep(A, B, C, ld, 65, 2, 64, D, need, None) == ERR_SHAPE
