@@ -85,7 +85,8 @@ enum {
     CONVROT_ERR_SHAPE = 2,     /* negative size, k % 256 != 0, k > 133120, ...   */
     CONVROT_ERR_ALIGN = 3,     /* a pointer is not 16-byte aligned               */
     CONVROT_ERR_WORKSPACE = 4, /* workspace NULL or smaller than required        */
-    CONVROT_ERR_LAUNCH = 5     /* the kernel launch failed (see hipGetLastError) */
+    CONVROT_ERR_LAUNCH = 5,    /* the kernel launch failed (see hipGetLastError) */
+    CONVROT_ERR_SCRATCH = 6    /* too large for convrot_linear_noalloc's scratch  */
 };
 
 #define CONVROT_GROUP 256
@@ -136,6 +137,26 @@ size_t convrot_workspace_bytes(int64_t m, int64_t k);
 int convrot_linear(const uint16_t* x, int64_t m, int64_t k,
                    const int8_t* q_w, const float* s_w, int64_t n,
                    uint16_t* y, void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same linear for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid allocation):
+ * it takes no workspace and calls no allocator.  Its q_x / s_x (the
+ * workspace of convrot_linear, m * k + 4 * m bytes) live in a fixed array of
+ * CONVROT_NOALLOC_SCRATCH_BYTES in the library's device code, which every GPU
+ * the library runs this call on holds until the process ends; the array's
+ * device address is looked up once per device on the first call there.
+ * Arguments, checks, results and errors are those of convrot_linear, except:
+ *   - m * k + 4 * m > CONVROT_NOALLOC_SCRATCH_BYTES returns
+ *     CONVROT_ERR_SCRATCH before anything is enqueued (use convrot_linear);
+ *   - every call on one GPU uses that GPU's one array, so calls on one GPU
+ *     whose executions overlap (different streams, no ordering between them)
+ *     race on it and give unspecified outputs; calls on one stream are
+ *     ordered and safe.  Nothing in the array needs to start at zero: each
+ *     call writes q_x and s_x before it reads them.                          */
+#define CONVROT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int convrot_linear_noalloc(const uint16_t* x, int64_t m, int64_t k,
+                           const int8_t* q_w, const float* s_w, int64_t n,
+                           uint16_t* y, void* stream);
 
 /* The fc1 ConvRot linear with SwiGLU fused into its epilogue (h3-rs README,
  * "Speed"; Minimax_h3_hybrid model card, "Checkpoints").

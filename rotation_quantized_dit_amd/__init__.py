@@ -20,7 +20,9 @@ from ._lib import (  # noqa: F401
     gemm_dequant,
     gemm_s32,
     gemm_swiglu,
+    NOALLOC_SCRATCH_BYTES,
     linear,
+    linear_noalloc,
     linear_swiglu,
     lora_add,
     load_library,

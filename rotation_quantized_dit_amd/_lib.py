@@ -20,7 +20,10 @@ LIB_PATH = os.path.join(HERE, "libconvrot.so")
 GROUP = 256
 MAX_K = 133120
 
-OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH = range(6)
+OK, ERR_NULL, ERR_SHAPE, ERR_ALIGN, ERR_WORKSPACE, ERR_LAUNCH, ERR_SCRATCH = range(7)
+
+# the fixed device array convrot_linear_noalloc uses as its workspace
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 SYMBOLS = (
     "convrot_quantize_weight", "convrot_rotate_quant_act", "convrot_workspace_bytes",
@@ -29,7 +32,7 @@ SYMBOLS = (
     "convrot_lora_add", "convrot_merge_workspace_bytes", "convrot_merge_lora", "convrot_status_string",
     "convrot_attention_workspace", "convrot_attention_prep", "convrot_attention_prepared",
     "convrot_attention", "convrot_mx_quantize_act", "convrot_mx_quantize_weight", "convrot_mx_gemm",
-    "convrot_mx_workspace_bytes", "convrot_mx_linear",
+    "convrot_mx_workspace_bytes", "convrot_mx_linear", "convrot_linear_noalloc",
 )
 
 ATTN_HEAD_DIM = 128
@@ -63,6 +66,7 @@ def load_library() -> ctypes.CDLL:
             "convrot_workspace_bytes": ([I64, I64], SZ),
             "convrot_linear": ([P, I64, I64, P, P, I64, P, P, SZ, P], I),
             "convrot_linear_swiglu": ([P, I64, I64, P, P, I64, P, P, SZ, P], I),
+            "convrot_linear_noalloc": ([P, I64, I64, P, P, I64, P, P], I),
             "convrot_gemm_dequant": ([P, P, P, P, I64, I64, I64, P, P], I),
             "convrot_gemm_swiglu": ([P, P, P, P, I64, I64, I64, P, P], I),
             "convrot_gemm_s32": ([P, P, I64, I64, I64, P, P], I),
@@ -201,6 +205,23 @@ def linear(x: torch.Tensor, q_w: torch.Tensor, s_w: torch.Tensor, out=None, work
     _check("convrot_linear", load_library().convrot_linear(
         x.data_ptr(), m, k, q_w.data_ptr(), s_w.data_ptr(), n, y.data_ptr(), ws.data_ptr(),
         ws.numel(), _stream()))
+    return y
+
+
+def linear_noalloc(x: torch.Tensor, q_w: torch.Tensor, s_w: torch.Tensor, out=None):
+    """convrot_linear_noalloc: the ConvRot linear with the library's own device
+    scratch as its workspace (m k + 4 m <= NOALLOC_SCRATCH_BYTES); the library
+    allocates nothing (out is allocated here unless passed)."""
+    _dev(x, "x", torch.bfloat16, 2)
+    _dev(q_w, "q_w", torch.int8, 2)
+    _dev(s_w, "s_w", torch.float32, 1)
+    m, k = x.shape
+    n = q_w.shape[0]
+    if q_w.shape[1] != k or s_w.shape[0] != n:
+        raise ValueError("shape mismatch: x %s, q_w %s, s_w %s" % (tuple(x.shape), tuple(q_w.shape), tuple(s_w.shape)))
+    y = _out(out, (m, n), torch.bfloat16, x, "out")
+    _check("convrot_linear_noalloc", load_library().convrot_linear_noalloc(
+        x.data_ptr(), m, k, q_w.data_ptr(), s_w.data_ptr(), n, y.data_ptr(), _stream()))
     return y
 
 

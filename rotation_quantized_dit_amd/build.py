@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 ROOT = os.path.dirname(HERE)
 LIB = os.path.join(HERE, "libconvrot.so")
 SOURCES = ["convrot_api.cpp", "rotate_quant.hip", "gemm_i8.hip", "weight_ops.hip", "attention.hip", "mx_quant.hip",
-           "gemm_mx.hip"]
+           "gemm_mx.hip", "noalloc.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

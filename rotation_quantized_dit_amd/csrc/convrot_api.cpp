@@ -68,6 +68,9 @@ const char* convrot_status_string(int status) {
         case CONVROT_ERR_ALIGN: return "a pointer is not 16-byte aligned";
         case CONVROT_ERR_WORKSPACE: return "workspace is NULL or smaller than convrot_workspace_bytes(m, k)";
         case CONVROT_ERR_LAUNCH: return "kernel launch failed (is the device gfx950?)";
+        case CONVROT_ERR_SCRATCH:
+            return "m * k + 4 * m exceeds the built-in scratch of convrot_linear_noalloc "
+                   "(CONVROT_NOALLOC_SCRATCH_BYTES); use convrot_linear with a workspace";
         default: return "unknown status";
     }
 }
@@ -196,14 +199,25 @@ int convrot_gemm_swiglu(const int8_t* q_x, const float* s_x, const int8_t* q_w, 
                                          (hipStream_t)stream));
 }
 
-static int linear_common(const uint16_t* x, int64_t m, int64_t k, const int8_t* q_w,
-                         const float* s_w, int64_t n, int64_t n_rows_w, uint16_t* y,
-                         void* workspace, size_t workspace_bytes, bool swiglu, void* stream) {
+}  // extern "C"
+
+namespace convrot {
+
+int linear_args(const uint16_t* x, int64_t m, int64_t k, const int8_t* q_w, const float* s_w,
+                int64_t n, int64_t n_rows_w, const uint16_t* y) {
     if (n < 0 || n > (int64_t)INT32_MAX / 2) return CONVROT_ERR_SHAPE;
     int st;
     if ((st = check_gemm_shape(m, n, n_rows_w, k))) return st;
     if (m == 0 || n == 0) return CONVROT_OK;
-    if ((st = check_gemm_ptrs(x, nullptr, false, q_w, s_w, true, y))) return st;
+    return check_gemm_ptrs(x, nullptr, false, q_w, s_w, true, y);
+}
+
+int linear_common(const uint16_t* x, int64_t m, int64_t k, const int8_t* q_w, const float* s_w,
+                  int64_t n, int64_t n_rows_w, uint16_t* y, void* workspace, size_t workspace_bytes,
+                  bool swiglu, void* stream) {
+    int st;
+    if ((st = linear_args(x, m, k, q_w, s_w, n, n_rows_w, y))) return st;
+    if (m == 0 || n == 0) return CONVROT_OK;
     if (!workspace || workspace_bytes < ws_bytes(m, k)) return CONVROT_ERR_WORKSPACE;
     if (!aligned16(workspace)) return CONVROT_ERR_ALIGN;
     int8_t* q_x = (int8_t*)workspace;
@@ -214,16 +228,20 @@ static int linear_common(const uint16_t* x, int64_t m, int64_t k, const int8_t* 
                                          s_w, m, n, k, y, s));
 }
 
+}  // namespace convrot
+
+extern "C" {
+
 int convrot_linear(const uint16_t* x, int64_t m, int64_t k, const int8_t* q_w, const float* s_w,
                    int64_t n, uint16_t* y, void* workspace, size_t workspace_bytes, void* stream) {
-    return linear_common(x, m, k, q_w, s_w, n, n, y, workspace, workspace_bytes, false, stream);
+    return convrot::linear_common(x, m, k, q_w, s_w, n, n, y, workspace, workspace_bytes, false, stream);
 }
 
 int convrot_linear_swiglu(const uint16_t* x, int64_t m, int64_t k, const int8_t* q_w,
                           const float* s_w, int64_t i, uint16_t* y, void* workspace,
                           size_t workspace_bytes, void* stream) {
     if (i < 0 || i > (int64_t)INT32_MAX / 2) return CONVROT_ERR_SHAPE;
-    return linear_common(x, m, k, q_w, s_w, i, 2 * i, y, workspace, workspace_bytes, true, stream);
+    return convrot::linear_common(x, m, k, q_w, s_w, i, 2 * i, y, workspace, workspace_bytes, true, stream);
 }
 
 }  // extern "C"

@@ -24,6 +24,17 @@ hipError_t launch_dequantize_weight(const int8_t* q, const float* s, int64_t n, 
 hipError_t launch_lora_add(float* w, int64_t n, int64_t k, const float* b, const float* a,
                            int64_t rank, float scale, hipStream_t stream);
 
+// The ConvRot linear behind convrot_linear / convrot_linear_swiglu (in
+// convrot_api.cpp): linear_args validates sizes and pointers exactly as those
+// entry points do (CONVROT_OK also for an empty call); linear_common validates
+// and then runs rotate+quantize into the workspace and the GEMM (n_rows_w is
+// n, or 2n with swiglu).  Both return a CONVROT_* status.
+int linear_args(const uint16_t* x, int64_t m, int64_t k, const int8_t* q_w, const float* s_w,
+                int64_t n, int64_t n_rows_w, const uint16_t* y);
+int linear_common(const uint16_t* x, int64_t m, int64_t k, const int8_t* q_w, const float* s_w,
+                  int64_t n, int64_t n_rows_w, uint16_t* y, void* workspace, size_t workspace_bytes,
+                  bool swiglu, void* stream);
+
 // K-GEMM: int8 x int8 -> int32 on MFMA with one of three epilogues.
 enum class Epilogue { S32, BF16, SWIGLU };
 

@@ -49,7 +49,7 @@ def test_library_exports_every_declared_symbol(L):
 
 def test_status_strings(L):
     from rotation_quantized_dit_amd import _lib
-    for st in range(6):
+    for st in range(7):
         s = _lib.status_string(st)
         assert isinstance(s, str) and s
     assert _lib.status_string(0) == "ok"
@@ -267,3 +267,27 @@ def test_c_abi_check_source_compiles():
     """tests/c_abi_check.c (the C-side check run on the GPU) is valid C11."""
     from tests import c_abi_build
     c_abi_build.compile_only("c")
+
+
+def test_linear_noalloc_validation(L):
+    """convrot_linear_noalloc: the checks of convrot_linear, then the size bound
+    of its built-in scratch (m k + 4 m bytes), all on the host before any HIP
+    call; empty calls are no-ops."""
+    from rotation_quantized_dit_amd._lib import (ERR_ALIGN, ERR_NULL, ERR_SCRATCH, ERR_SHAPE, NOALLOC_SCRATCH_BYTES,
+                                                 OK)
+    f = L.convrot_linear_noalloc
+    assert NOALLOC_SCRATCH_BYTES == 64 << 20
+    for k in (0, 100, 133376):
+        assert f(A, 4, k, B, C, 4, D, None) == ERR_SHAPE, k
+    assert f(A, -1, 256, B, C, 4, D, None) == ERR_SHAPE
+    assert f(None, 0, 256, None, None, 4, None, None) == OK
+    assert f(None, 4, 256, None, None, 0, None, None) == OK
+    assert f(None, 4, 256, B, C, 4, D, None) == ERR_NULL
+    assert f(MIS, 4, 256, B, C, 4, D, None) == ERR_ALIGN
+    # the largest m that fits at k = 5376, and the next one
+    k = 5376
+    m_max = NOALLOC_SCRATCH_BYTES // (k + 4)
+    assert m_max * (k + 4) <= NOALLOC_SCRATCH_BYTES < (m_max + 1) * (k + 4)
+    assert f(A, m_max + 1, k, B, C, 16, D, None) == ERR_SCRATCH
+    assert f(A, 1 << 20, 14336, B, C, 16, D, None) == ERR_SCRATCH
+    assert "scratch" in L.convrot_status_string(ERR_SCRATCH).decode()
