@@ -44,7 +44,9 @@
 // the LDS destination, is passed as an input operand, so the compiler knows
 // it is set.
 //
-// Main loop (one stage = two k-steps of 12 MFMAs per wave), one basic block:
+// Main loop (one stage = two k-steps of 12 MFMAs per wave), unrolled over
+// the four slots of the ring so that every LDS offset is an immediate (K is
+// a multiple of 256, so the stage count is a multiple of four):
 //   - the MFMAs run in a fixed order (A0 x B0..B3, then A1/A2 alternating
 //     over B0..B3), and each fragment register is refilled with the next
 //     k-step's fragment right after its last use, which spreads the seven
@@ -56,8 +58,8 @@
 //   - after the barrier the current slot is refilled with the stage four
 //     ahead: three copies spread over the rest of that k-step, the last two
 //     in the next stage's first k-step.
-// Past the last stage the copies are still issued (so every iteration is the
-// same basic block and the vmcnt counts stay uniform) but with the voffset
+// Past the last stage the copies are still issued (so every stage has the
+// same shape and the vmcnt counts stay uniform) but with the voffset
 // pushed beyond the buffer's range: the hardware returns zeros without a
 // memory access and they land in slots no one reads again.
 //
@@ -67,10 +69,12 @@
 // run together on one XCD share A and B panels in that XCD's L2, and the
 // weight panels, re-read once per group, stay in the 256 MB Infinity Cache.
 //
-// Ragged edges: rows past M or N are clamped to the last row for loading and
-// masked at the store.
+// Ragged edges: a panel's rows past M or N lie past its buffer resource's
+// range and load as zeros; their outputs are masked at the store.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "fixed_math.h"
 #include "kernels.h"
@@ -212,32 +216,26 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     const int m0 = tile.tm * BM;
     const int rows_a = (M - m0) < BM ? (M - m0) : BM;
 
-    // Epilogue scales, loaded before the main loop so that their latency is
-    // hidden: s_x of the tile's row tid into a register (parked in LDS after
-    // the loop, where the ring was), and s_w of the lane's 8 output columns
-    // (gate and up columns for SwiGLU).
+    // Epilogue scales: s_x of the tile's row tid into a register before the
+    // main loop (parked in LDS after it, where the ring was); s_w of the
+    // lane's 8 output columns is loaded after the loop (fewer registers live
+    // across it).
     constexpr int EPI_CG = EP == Epilogue::SWIGLU ? 8 : 16;   // column groups per wave row
     const int epi_cg = lane % EPI_CG;
     const int epi_ro = lane / EPI_CG;
     const int epi_col0 = EP == Epilogue::SWIGLU ? tile.tn * (BN / 2) + 64 * wn + 8 * epi_cg
                                                 : tile.tn * BN + 128 * wn + 8 * epi_cg;
     float sx_own = 0.0f;
-    float swa[8], swb[8];
     if constexpr (EP != Epilogue::S32) {
         if (tid < BM) sx_own = sx[tid < rows_a ? m0 + tid : M - 1];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int c = (epi_col0 + e) < N ? (epi_col0 + e) : (N - 1);
-            swa[e] = sw[c];
-            swb[e] = EP == Epilogue::SWIGLU ? sw[N + c] : 0.0f;
-        }
     }
 
     // Copy sources.  Copy i < MA of wave w fills A slab rows 16 (MA w + i) ..
     // +15 of a stage; copy MA + i (i = 0, 1) fills B slab rows 32 w + 16 i ..
     // +15.  Lane l writes row (l / 4) of its 16 at chunk position l % 4,
     // which holds logical chunk (l % 4) ^ swz(row).  Offsets are relative to a
-    // per-panel buffer resource (the tile's A rows; its gate rows; its up rows).
+    // per-panel buffer resource (the tile's A rows; its gate rows; its up
+    // rows), whose range ends at the panel's last row.
     int b_first;   // first weight row of this tile (gate rows for SwiGLU)
     if constexpr (EP == Epilogue::SWIGLU)
         b_first = tile.tn * (BN / 2);
@@ -254,30 +252,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     } else {
         rsrc_b = rsrc_words(B + (int64_t)b_first * K, (uint32_t)rows_b * (uint32_t)K);
     }
-    uint32_t voff[COPIES];
-#pragma unroll
-    for (int i = 0; i < COPIES; ++i) {
-        const int rr = i < MA ? 16 * (MA * wave + i) + (lane >> 2)           // A slab row
-                              : 32 * wave + 16 * (i - MA) + (lane >> 2);    // B slab row
-        const int c = (lane & 3) ^ swz(rr);
-        int src_row;
-        if (i < MA) {
-            src_row = rr < rows_a ? rr : rows_a - 1;
-        } else if constexpr (EP == Epilogue::SWIGLU) {
-            const int j = rr & 127;   // the gate or up row of output column b_first + j
-            src_row = j < rows_b ? j : rows_b - 1;
-        } else {
-            src_row = rr < rows_b ? rr : rows_b - 1;
-        }
-        voff[i] = (uint32_t)src_row * (uint32_t)K + 16u * (uint32_t)c;
-    }
+    // Row r of a panel is read at r K + its swizzled chunk.  Rows past the
+    // panel's last row lie past the buffer's range and read as zeros (their
+    // outputs are masked at the store).  A wave's copies are 16 rows apart
+    // and share one swizzle, ((r >> 2) & 3) = ((lane >> 4) & 3).
+    const uint32_t chunk = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+    const uint32_t voff_a = (uint32_t)(16 * MA * wave + (lane >> 2)) * (uint32_t)K + chunk;
+    const uint32_t voff_b = (uint32_t)(32 * (EP == Epilogue::SWIGLU ? (wave & 3) : wave) + (lane >> 2)) * (uint32_t)K + chunk;
+    const uint32_t row16 = 16u * (uint32_t)K;
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int8_t*)lds);
     // copy i of the stage at K byte soff into ring slot `slot` (oob: 0 or OOB)
     auto issue = [&](int i, uint32_t soff, uint32_t oob, int slot) {
         const uint32_t dst = i < MA ? lds_base + slot * STAGE_BYTES + 1024 * (MA * wave + i)
                                     : lds_base + slot * STAGE_BYTES + A_STAGE + 2048 * wave + 1024 * (i - MA);
-        copy16(i < MA ? rsrc_a : rsrc_b, dst, voff[i] + oob, soff);
+        const uint32_t vo = i < MA ? voff_a + (uint32_t)i * row16 : voff_b + (uint32_t)(i - MA) * row16;
+        copy16(i < MA ? rsrc_a : rsrc_b, dst, vo + oob, soff);
     };
 
     // LDS rows of this lane's fragments: A blocks a < MA (rows of the wave's
@@ -356,19 +346,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     constexpr int CS[COPIES_NOW] = {4, 7, 10};
     constexpr int BARRIER_AFTER = 3;
 
-    int slot = 0;
-    uint32_t soff = (uint32_t)STAGES * BK;
-    // Before the first refill, the deferred copies of stage STAGES - 1 are
-    // issued once more (the same bytes into a slot no one reads before they
-    // land), so that every iteration has the same shape.
-    int prev_slot = STAGES - 1;
-    uint32_t prev_soff = (uint32_t)(STAGES - 1) * BK, prev_oob = 0;
-    for (int kt = 0; kt < KT; ++kt) {
-        const int next = slot + 1 == STAGES ? 0 : slot + 1;
+    // One stage with its ring slot known at compile time (every LDS offset an
+    // immediate); K is a multiple of 256, so the stage count is a multiple
+    // of STAGES and the loop runs whole rounds.
+    static_assert(256 % (STAGES * BK) == 0, "whole rounds of STAGES stages");
+    auto stage = [&](auto slot_c, int kt) {
+        constexpr int slot = decltype(slot_c)::value;
+        constexpr int next = slot + 1 == STAGES ? 0 : slot + 1;
+        constexpr int prev_slot = slot == 0 ? STAGES - 1 : slot - 1;
         const uint32_t oob = kt + STAGES < KT ? 0u : OOB;
+        // the deferred copies belong to the previous stage's refill (before the
+        // first refill: stage STAGES - 1 again, the same bytes into its slot)
+        const uint32_t prev_soff = kt > 0 ? (uint32_t)(kt - 1 + STAGES) * BK : (uint32_t)(STAGES - 1) * BK;
+        const uint32_t prev_oob = kt > 0 && kt - 1 + STAGES >= KT ? OOB : 0u;
+        const uint32_t soff = (uint32_t)(kt + STAGES) * BK;
         const int8_t* cur = lds + slot * STAGE_BYTES;
         const int8_t* nxt = lds + next * STAGE_BYTES;
-        // k-step 0 of stage kt; refills from k-step 1 of the same slot
 #pragma unroll
         for (int i = 0; i < 12; ++i) {
             __builtin_amdgcn_sched_barrier(0);
@@ -377,15 +370,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
             if (i == 0) issue(COPIES_NOW, prev_soff, prev_oob, prev_slot);
             if (i == 6) issue(COPIES_NOW + 1, prev_soff, prev_oob, prev_slot);
         }
-        // k-step 1: the first slots run on fragments already in registers
 #pragma unroll
         for (int i = 0; i <= BARRIER_AFTER; ++i) {
             __builtin_amdgcn_sched_barrier(0);
             mfma(i);
         }
         __builtin_amdgcn_sched_barrier(0);
-        // Stage kt + 1 has landed: this wave's copies of it (only the two
-        // later stages' copies may still be in flight), then every wave's.
         wait_vmcnt<(STAGES - 2) * COPIES>();
         lds_barrier();
 #pragma unroll
@@ -403,12 +393,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                 if (CS[j] == i) issue(j, soff, oob, slot);
         }
         __builtin_amdgcn_sched_barrier(0);
-        prev_slot = slot;
-        prev_soff = soff;
-        prev_oob = oob;
-        slot = next;
-        soff += BK;
+    };
+    static_assert(STAGES == 4, "rounds of four stages");
+    for (int kt = 0; kt < KT; kt += 4) {
+        stage(std::integral_constant<int, 0>{}, kt);
+        stage(std::integral_constant<int, 1>{}, kt + 1);
+        stage(std::integral_constant<int, 2>{}, kt + 2);
+        stage(std::integral_constant<int, 3>{}, kt + 3);
     }
+    const int prev_slot = STAGES - 1;
+    const uint32_t prev_soff = (uint32_t)(KT - 1 + STAGES) * BK;
     // the deferred copies of the last refill (out of range), then no copy may
     // still be writing the ring, which the epilogue reuses
 #pragma unroll
@@ -422,6 +416,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     // ring, then reads them back row-contiguous: every lane takes 8
     // consecutive columns of one row, applies the scales and the epilogue math
     // in a compact loop, and writes one 16-byte store.
+    // s_w of the lane's 8 output columns (gate and up columns for SwiGLU)
+    float swa[8], swb[8];
+    if constexpr (EP != Epilogue::S32) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int c = (epi_col0 + e) < N ? (epi_col0 + e) : (N - 1);
+            swa[e] = sw[c];
+            swb[e] = EP == Epilogue::SWIGLU ? sw[N + c] : 0.0f;
+        }
+    }
     lds_barrier();   // every wave is done reading the ring
     float* sx_lds = reinterpret_cast<float*>(lds + SX_OFFSET);
     if constexpr (EP != Epilogue::S32) {

@@ -21,6 +21,16 @@
 // for 64 x 128) and the 384-row tile copies 17 % fewer bytes per flop than a
 // 256-row one; both measured about 8 % faster on the FFN-input shape.
 //
+// The main loop has the int8 kernel's schedule: copies issued from inline
+// assembly (so the compiler does not drain them before every fragment read),
+// a fixed MFMA order with each fragment register (and its block scale)
+// refilled right after its last use, the stage barrier after the fourth MFMA
+// of the second k-step, the refill copies spread over that k-step, copies
+// past the last stage pushed out of the buffer's range, and the stage loop
+// unrolled over the ring's three slots so that every LDS offset is an
+// immediate (without that the slot arithmetic needs registers the loop does
+// not have).
+//
 // Each stage also carries the tile's scale words (one 32-bit word per row:
 // the 4 block scales of its 128 elements), 384 + 256 words copied as three
 // 1 KiB direct loads: waves 0 and 1 take the A rows (the upper half of wave
@@ -30,10 +40,12 @@
 // spare 1 KiB of LDS.  For k-step s a lane reads the one byte it needs,
 // block 2 s + lane / 32 of its row, with a byte load from LDS.
 //
-// Ragged rows are clamped to the last row for loading and masked at the
-// store; K must be a multiple of 128.
+// Ragged rows lie past their panel's buffer range, load as zeros and are
+// masked at the store; K must be a multiple of 128.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "fixed_math.h"
 #include "kernels.h"
@@ -69,7 +81,6 @@ typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
@@ -86,16 +97,26 @@ __device__ __forceinline__ void lds_barrier() {
     asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ void copy16(__amdgpu_buffer_rsrc_t rsrc, uint8_t* dst, uint32_t voff,
-                                       uint32_t soff) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)dst, 16, voff, soff, 0, 0);
-#endif
+// Buffer resource words over [base, base + bytes) (raw, no stride; gfx9
+// dword 3), uniform across the wave.
+__device__ __forceinline__ v4u rsrc_words(const void* base, uint32_t bytes) {
+    const uint64_t b = (uint64_t)base;
+    v4u r;
+    r.x = __builtin_amdgcn_readfirstlane((uint32_t)b);
+    r.y = __builtin_amdgcn_readfirstlane((uint32_t)(b >> 32));
+    r.z = __builtin_amdgcn_readfirstlane(bytes);
+    r.w = 0x00020000u;
+    return r;
 }
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
-    return __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, (int)bytes, 0x00020000);
+// One direct copy: 64 lanes x 16 bytes from rsrc + voff + soff into LDS at
+// lds_addr + 16 * lane (M0 holds the LDS address; no VGPR is written).
+__device__ __forceinline__ void dma16(v4u rsrc, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+    asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %0, %1, %2 offen lds"
+                 :: "v"(voff), "s"(rsrc), "s"(soff), "{m0}"(lds_addr));
 }
+// Past-the-end offset for copies of stages beyond the last: beyond any
+// buffer's num_records (< 2^31), so the load returns zeros and reads nothing.
+constexpr uint32_t OOB = 0x80000000u;
 
 struct Tile {
     int tm, tn;
@@ -133,35 +154,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
     const int KB = K / 2;
     const int KT = K / 128;
 
-    const __amdgpu_buffer_rsrc_t rsrc_a = make_rsrc(A + (int64_t)m0 * KB, (uint32_t)rows_a * (uint32_t)KB);
-    const __amdgpu_buffer_rsrc_t rsrc_b = make_rsrc(B + (int64_t)n0 * KB, (uint32_t)rows_b * (uint32_t)KB);
+    const v4u rsrc_a = rsrc_words(A + (int64_t)m0 * KB, (uint32_t)rows_a * (uint32_t)KB);
+    const v4u rsrc_b = rsrc_words(B + (int64_t)n0 * KB, (uint32_t)rows_b * (uint32_t)KB);
     // scale copies: waves 0 and 1 the tile's A scale words (rows 256 w + 4 l .. +3; the upper half of
     // wave 1's copy reads rows past the tile into the unused end of the A scale area), wave 2 the B
-    // words; waves 3-7 issue the same instruction on an empty resource into a spare area (no branch)
-    const __amdgpu_buffer_rsrc_t rsrc_s =
-        wave < 2 ? make_rsrc(SA + (int64_t)m0 * 4, (uint32_t)((int64_t)(KT - 1) * M * 4 + rows_a * 4))
-        : wave == 2 ? make_rsrc(SB + (int64_t)n0 * 4, (uint32_t)((int64_t)(KT - 1) * N * 4 + rows_b * 4))
-                    : make_rsrc(SB, 0u);
+    // words; waves 3-7 issue the same instruction on an empty resource into a spare area
+    const v4u rsrc_s =
+        wave < 2 ? rsrc_words(SA + (int64_t)m0 * 4, (uint32_t)((int64_t)(KT - 1) * M * 4 + rows_a * 4))
+        : wave == 2 ? rsrc_words(SB + (int64_t)n0 * 4, (uint32_t)((int64_t)(KT - 1) * N * 4 + rows_b * 4))
+                    : rsrc_words(SB, 0u);
     const uint32_t chunk_stride = wave < 2 ? (uint32_t)M * 4u : wave == 2 ? (uint32_t)N * 4u : 0u;
     const uint32_t voff_s = (uint32_t)(wave < 2 ? 1024 * wave : 0) + 16u * (uint32_t)lane;
     const int s_dst = wave < 2 ? A_STAGE + B_STAGE + 1024 * wave
                       : wave == 2 ? A_STAGE + B_STAGE + SA_BYTES : SPARE;
-    uint32_t voff[MA + 2];
-#pragma unroll
-    for (int i = 0; i < MA + 2; ++i) {
-        const int rr = i < MA ? 16 * (MA * wave + i) + (lane >> 2) : 32 * wave + 16 * (i - MA) + (lane >> 2);
-        const int lim = i < MA ? rows_a : rows_b;
-        const int src_row = rr < lim ? rr : lim - 1;
-        voff[i] = (uint32_t)src_row * (uint32_t)KB + 16u * (uint32_t)((lane & 3) ^ swz(rr));
-    }
-    auto issue = [&](int kt, int slot) {
-        uint8_t* st = lds + slot * STAGE_BYTES;
+    // Row rr of a copy is read at rr * KB + its swizzled chunk; rows past the
+    // tile's last row lie past the buffer's range and read as zeros (their
+    // outputs are masked at the store).  Consecutive copies of a wave are 16
+    // rows apart and share the swizzle ((rr >> 2) & 3 = (lane >> 4) & 3).
+    const uint32_t chunk = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+    const uint32_t voff_a = (uint32_t)(16 * MA * wave + (lane >> 2)) * (uint32_t)KB + chunk;
+    const uint32_t voff_b = (uint32_t)(32 * wave + (lane >> 2)) * (uint32_t)KB + chunk;
+    const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)lds);
+    // copy i of stage kt into slot: i < MA A rows, MA, MA + 1 B rows, MA + 2 the scale words
+    auto issue = [&](int i, int kt, uint32_t oob, int slot) {
+        const uint32_t st = lds_base + slot * STAGE_BYTES;
         const uint32_t soff = (uint32_t)kt * BK;
-#pragma unroll
-        for (int i = 0; i < MA; ++i) copy16(rsrc_a, st + 16 * 64 * MA * wave + 1024 * i, voff[i], soff);
-        copy16(rsrc_b, st + A_STAGE + 32 * 64 * wave, voff[MA], soff);
-        copy16(rsrc_b, st + A_STAGE + 32 * 64 * wave + 1024, voff[MA + 1], soff);
-        copy16(rsrc_s, (wave < 3 ? st : lds) + s_dst, voff_s, (uint32_t)kt * chunk_stride);
+        if (i < MA) dma16(rsrc_a, st + 16 * 64 * MA * wave + 1024 * i, voff_a + (16u * i * KB + oob), soff);
+        else if (i < MA + 2)
+            dma16(rsrc_b, st + A_STAGE + 32 * 64 * wave + 1024 * (i - MA), voff_b + (16u * (i - MA) * KB + oob), soff);
+        else dma16(rsrc_s, (wave < 3 ? st : lds_base) + s_dst, voff_s + oob, (uint32_t)kt * chunk_stride);
     };
 
     v16f acc[MA][4];
@@ -176,86 +198,118 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
     // row of a lane is (lane >> 2) & 3 (the rows differ by multiples of 32),
     // so each operand needs one lane offset per k-step, the blocks following
     // at fixed distances (2048 bytes per 32 code rows, 128 per 32 scale words).
-    const int sw = (lane >> 2) & 3;
+    const int sw = swz(lane & 31);
     const int a_lane = (32 * MA * wm + (lane & 31)) * BK;
     const int b_lane = A_STAGE + (128 * wn + (lane & 31)) * BK;
-    const int sa_lane = A_STAGE + B_STAGE + 4 * (32 * MA * wm + (lane & 31)) + g;
-    const int sb_lane = A_STAGE + B_STAGE + SA_BYTES + 4 * (128 * wn + (lane & 31)) + g;
-    auto read_frags = [&](const uint8_t* st, int s, v4i (&af)[MA], v4i (&bf)[4], int (&sa)[MA], int (&sb)[4]) {
-        const int c = 16 * ((2 * s + g) ^ sw);
-        const uint8_t* pa = st + (a_lane + c);
-        const uint8_t* pb = st + (b_lane + c);
-#pragma unroll
-        for (int a = 0; a < MA; ++a) af[a] = *reinterpret_cast<const v4i*>(pa + 2048 * a);
-#pragma unroll
-        for (int b = 0; b < 4; ++b) bf[b] = *reinterpret_cast<const v4i*>(pb + 2048 * b);
-        const uint8_t* psa = st + sa_lane;
-        const uint8_t* psb = st + sb_lane;
-#pragma unroll
-        for (int a = 0; a < MA; ++a) sa[a] = psa[128 * a + 2 * s];
-#pragma unroll
-        for (int b = 0; b < 4; ++b) sb[b] = psb[128 * b + 2 * s];
-    };
-    auto mma = [&](const v4i (&af)[MA], const v4i (&bf)[4], const int (&sa)[MA], const int (&sb)[4]) {
-#pragma unroll
-        for (int a = 0; a < MA; ++a)
-#pragma unroll
-            for (int b = 0; b < 4; ++b) {
-                const v8i av = {af[a].x, af[a].y, af[a].z, af[a].w, 0, 0, 0, 0};
-                const v8i bv = {bf[b].x, bf[b].y, bf[b].z, bf[b].w, 0, 0, 0, 0};
-                acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[a][b], 4, 4, 0, sa[a], 0,
-                                                                            sb[b]);
-            }
-    };
+    // A row's scale word holds the block scales of its 128 elements; the
+    // lanes of half g use block 2 s + g in k-step s (one byte read).
+    const int sa_byte = A_STAGE + B_STAGE + 4 * (32 * MA * wm + (lane & 31)) + g;
+    const int sb_byte = A_STAGE + B_STAGE + SA_BYTES + 4 * (128 * wn + (lane & 31)) + g;
+    const int c0 = 16 * ((0 + g) ^ sw), c1 = 16 * ((2 + g) ^ sw);
 
 #pragma unroll
     for (int st = 0; st < STAGES; ++st)
-        if (st < KT) issue(st, st);
-    {
-        const int ahead = (KT - 1) < (STAGES - 1) ? (KT - 1) : (STAGES - 1);
-        if (ahead >= 2) wait_vmcnt<2 * COPIES>();
-        else if (ahead == 1) wait_vmcnt<COPIES>();
-        else wait_vmcnt<0>();
-    }
+#pragma unroll
+        for (int i = 0; i < COPIES; ++i) issue(i, st, st < KT ? 0u : OOB, st);
+    wait_vmcnt<(STAGES - 1) * COPIES>();
     lds_barrier();
 
-    int slot = 0;
-    int kt = 0;
     v4i fa[MA], fb[4];
     int sa[MA], sb[4];
-    // Steady state (a refill per stage) as straight-line code, so that the
-    // scheduling barriers hold the order: k-step 0's reads and MFMAs, k-step
-    // 1's reads, the wait for stage kt + 1 and the barrier, the refill, k-step
-    // 1's MFMAs.
-    for (; kt + STAGES < KT; ++kt) {
-        const int next = slot + 1 == STAGES ? 0 : slot + 1;
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(lds + slot * STAGE_BYTES, 0, fa, fb, sa, sb);
-        mma(fa, fb, sa, sb);
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(lds + slot * STAGE_BYTES, 1, fa, fb, sa, sb);
-        wait_vmcnt<COPIES>();
-        lds_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        issue(kt + STAGES, slot);
-        mma(fa, fb, sa, sb);
-        __builtin_amdgcn_sched_barrier(0);
-        slot = next;
+#pragma unroll
+    for (int a = 0; a < MA; ++a) {
+        fa[a] = *reinterpret_cast<const v4i*>(lds + a_lane + c0 + 2048 * a);
+        sa[a] = lds[sa_byte + 128 * a];
     }
-    for (; kt < KT; ++kt) {
-        const int next = slot + 1 == STAGES ? 0 : slot + 1;
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(lds + slot * STAGE_BYTES, 0, fa, fb, sa, sb);
-        mma(fa, fb, sa, sb);
-        __builtin_amdgcn_sched_barrier(0);
-        read_frags(lds + slot * STAGE_BYTES, 1, fa, fb, sa, sb);
-        wait_vmcnt<0>();
-        lds_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        mma(fa, fb, sa, sb);
-        __builtin_amdgcn_sched_barrier(0);
-        slot = next;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+        fb[b] = *reinterpret_cast<const v4i*>(lds + b_lane + c0 + 2048 * b);
+        sb[b] = lds[sb_byte + 128 * b];
     }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_sched_barrier(0);
+
+    constexpr int SA_[12] = {0, 0, 0, 0, 1, 2, 1, 2, 1, 2, 1, 2};
+    constexpr int SB_[12] = {0, 1, 2, 3, 0, 0, 1, 1, 2, 2, 3, 3};
+    auto mfma = [&](int i, int s) {
+        const int a = SA_[i], b = SB_[i];
+        const v8i av = {fa[a].x, fa[a].y, fa[a].z, fa[a].w, 0, 0, 0, 0};
+        const v8i bv = {fb[b].x, fb[b].y, fb[b].z, fb[b].w, 0, 0, 0, 0};
+        (void)s;
+        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[a][b], 4, 4, 0, sa[a], 0, sb[b]);
+    };
+    // refill after slot i with the fragments of k-step s of stage st (and, for
+    // k-step 0 of the next stage, the scale words)
+    auto refill = [&](int i, const uint8_t* st, int s) {
+        const int c = s == 0 ? c0 : c1;
+        auto fa_ = [&](int a) {
+            fa[a] = *reinterpret_cast<const v4i*>(st + a_lane + c + 2048 * a);
+            sa[a] = st[sa_byte + 128 * a + 2 * s];
+        };
+        auto fb_ = [&](int b) {
+            fb[b] = *reinterpret_cast<const v4i*>(st + b_lane + c + 2048 * b);
+            sb[b] = st[sb_byte + 128 * b + 2 * s];
+        };
+        if (i == 3) fa_(0);
+        if (i == 5) fb_(0);
+        if (i == 7) fb_(1);
+        if (i == 9) fb_(2);
+        if (i == 11) {
+            fb_(3);
+            fa_(1);
+            fa_(2);
+        }
+    };
+    constexpr int CS[COPIES] = {4, 5, 6, 7, 8, 9};
+    constexpr int BARRIER_AFTER = 3;
+    // One stage with its ring slot known at compile time (every LDS offset an
+    // immediate); the stage loop runs in rounds of STAGES.
+    auto stage = [&](auto slot_c, int kt) {
+        constexpr int slot = decltype(slot_c)::value;
+        constexpr int next = slot + 1 == STAGES ? 0 : slot + 1;
+        const uint32_t oob = kt + STAGES < KT ? 0u : OOB;
+        const uint8_t* cur = lds + slot * STAGE_BYTES;
+        const uint8_t* nxt = lds + next * STAGE_BYTES;
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(i, 0);
+            refill(i, cur, 1);
+        }
+#pragma unroll
+        for (int i = 0; i <= BARRIER_AFTER; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            mfma(i, 1);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        wait_vmcnt<(STAGES - 2) * COPIES>();
+        lds_barrier();
+#pragma unroll
+        for (int i = 0; i < 12; ++i) {
+            __builtin_amdgcn_sched_barrier(0);
+            if (i > BARRIER_AFTER) mfma(i, 1);
+            if (i == BARRIER_AFTER) {
+#pragma unroll
+                for (int j = 0; j <= BARRIER_AFTER; ++j) refill(j, nxt, 0);
+            } else if (i > BARRIER_AFTER) {
+                refill(i, nxt, 0);
+            }
+#pragma unroll
+            for (int j = 0; j < COPIES; ++j)
+                if (CS[j] == i) issue(j, kt + STAGES, oob, slot);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+    static_assert(STAGES == 3, "rounds of three stages");
+    int kt = 0;
+    for (; kt + 3 <= KT; kt += 3) {
+        stage(std::integral_constant<int, 0>{}, kt);
+        stage(std::integral_constant<int, 1>{}, kt + 1);
+        stage(std::integral_constant<int, 2>{}, kt + 2);
+    }
+    if (kt < KT) stage(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < KT) stage(std::integral_constant<int, 1>{}, kt + 1);
+    wait_vmcnt<0>();
 
     lds_barrier();
     float* stash = reinterpret_cast<float*>(lds + wave * STASH_WAVE_BYTES);
