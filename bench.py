@@ -188,6 +188,127 @@ def attention_bench(torch, cr, dev, steps):
     return res
 
 
+def qkv_bench(torch, cr, dev, steps):
+    """The fused QKV projection, 4096 x 5376 x 16128 (the QKV workload: 1 %
+    outlier channels x30): the rotate+quantize pass, the GEMM with its bf16
+    dequant epilogue, and the whole convrot_linear call, each timed on its own
+    with HIP events on the launch stream."""
+    import workloads
+    log("qkv: generating inputs")
+    d = workloads.make_linear("qkv")
+    x = torch.from_numpy(d["x"].view(np.int16)).view(torch.bfloat16).to(dev)
+    w = torch.from_numpy(d["w"]).to(dev)
+    del d
+    M, K = x.shape
+    N = w.shape[0]
+    qw, sw = cr.quantize_weight(w)
+    del w
+    qx = torch.empty((M, K), dtype=torch.int8, device=dev)
+    sx = torch.empty((M,), dtype=torch.float32, device=dev)
+    y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(cr.workspace_bytes(M, K), dtype=torch.uint8, device=dev)
+    n = max(5, min(steps, 20))
+
+    def time_it(fn):
+        for _ in range(3):
+            fn()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
+        ev[0].record()
+        for i in range(n):
+            fn()
+            ev[i + 1].record()
+        torch.cuda.synchronize()
+        t = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(n)])
+        return float(np.median(t)), float(t.min())
+    rot, rot_min = time_it(lambda: cr.rotate_quant_act(x, qx, sx))
+    gemm, gemm_min = time_it(lambda: cr.gemm_dequant(qx, sx, qw, sw, out=y))
+    lin, lin_min = time_it(lambda: cr.linear(x, qw, sw, out=y, workspace=ws))
+    ops = 2.0 * M * N * K
+    tiles = ((M + 383) // 384) * ((N + 255) // 256)
+    res = {"config": {"workload": "qkv: fused QKV projection", "m": M, "k": K, "n": N},
+           "rotate_quant": {"ms": round(rot, 4), "GB/s": round((3.0 * M * K + 4.0 * M) / (rot * 1e-3) / 1e9, 1)},
+           "gemm_dequant": {"ms": round(gemm, 4), "ms_min": round(gemm_min, 4),
+                            "TOPS": round(ops / (gemm * 1e-3) / 1e12, 1),
+                            "pct_int8_peak": round(100.0 * ops / (gemm * 1e-3) / 1e12 / PEAK_INT8_TOPS, 1)},
+           "linear_end_to_end": {"ms": round(lin, 4), "ms_min": round(lin_min, 4),
+                                 "TOPS": round(ops / (lin * 1e-3) / 1e12, 1),
+                                 "pct_int8_peak": round(100.0 * ops / (lin * 1e-3) / 1e12 / PEAK_INT8_TOPS, 1)},
+           "tiles": tiles, "rounds_of_256_cus": round(tiles / 256.0, 2)}
+    del x, qw, sw, qx, sx, y, ws
+    torch.cuda.empty_cache()
+    return res
+
+
+def sustained_clock(torch, fn, ops, seconds=2.5):
+    """The kernel launched back to back for about `seconds`, while `amd-smi`
+    samples the gfx clocks of the 8 XCDs and the socket power: the clock the
+    chip sustains under this kernel (the profiler's serialized dispatches run
+    it cooler and faster).  Returns None where amd-smi is not available."""
+    import shutil
+    import subprocess
+    import threading
+    if not shutil.which("amd-smi"):
+        return None
+    samples, stop = [], [False]
+
+    def sampler():
+        while not stop[0]:
+            try:
+                r = subprocess.run(["amd-smi", "metric", "--clock", "--power", "--json"], capture_output=True,
+                                   text=True, timeout=10)
+                samples.append((time.perf_counter(), r.stdout))
+            except Exception:       # a failed sample is skipped
+                time.sleep(0.1)
+    for _ in range(5):
+        fn()
+    torch.cuda.synchronize()
+    th = threading.Thread(target=sampler, daemon=True)
+    t0 = time.perf_counter()
+    th.start()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        for _ in range(10):
+            fn()
+        n += 10
+        torch.cuda.synchronize()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stop[0] = True
+    th.join(timeout=15)
+    ms = e0.elapsed_time(e1) / n
+    clocks, powers = [], []
+    for ts, out in samples:
+        if ts < t0 + 0.3 or ts > t1 - 0.1:      # skip samples taken while the load ramps or ends
+            continue
+        try:
+            data = json.loads(out)
+        except ValueError:
+            continue
+        gpus = data.get("gpu_data", data) if isinstance(data, dict) else data
+        for g in gpus if isinstance(gpus, list) else [gpus]:
+            clk = g.get("clock", {})
+            for key, v in clk.items():
+                if key.startswith("gfx_") and isinstance(v, dict) and isinstance(v.get("clk"), dict):
+                    val = v["clk"].get("value")
+                    if isinstance(val, (int, float)) and val > 0:
+                        clocks.append(float(val))
+            pw = g.get("power", {}).get("socket_power", {})
+            if isinstance(pw, dict) and isinstance(pw.get("value"), (int, float)):
+                powers.append(float(pw["value"]))
+    if not clocks:
+        return None
+    return {"clock_ghz": round(float(np.median(clocks)) / 1000.0, 3),
+            "clock_ghz_min": round(min(clocks) / 1000.0, 3), "clock_ghz_max": round(max(clocks) / 1000.0, 3),
+            "socket_power_w": round(float(np.median(powers)), 1) if powers else None,
+            "samples": len(clocks), "launches": n, "ms_per_launch": round(ms, 4),
+            "TOPS": round(ops / (ms * 1e-3) / 1e12, 1),
+            "source": "amd-smi metric --clock --power (gfx clock of each XCD, socket power), sampled while the "
+                      "kernel ran back to back for %.1f s" % (t1 - t0)}
+
+
 def hybrid_bench(torch, cr, dev, steps):
     """One block's four projections at 32464 tokens (the block chain: 32256
     video + 208 audio tokens), int8 ConvRot everywhere against the MXFP4
@@ -217,6 +338,7 @@ def hybrid_bench(torch, cr, dev, steps):
     qh = torch.empty((M, F), dtype=torch.int8, device=dev)
     sh = torch.empty((M,), dtype=torch.float32, device=dev)
     o4 = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
+    h_ = torch.empty((M, F), dtype=torch.bfloat16, device=dev)
     x1 = workloads.chain_outliers(x0, idx[0])
 
     def attn_stand_in():
@@ -225,8 +347,9 @@ def hybrid_bench(torch, cr, dev, steps):
 
     def run(variant, ev=None):
         rec = (lambda i: ev[i].record()) if ev else (lambda i: None)
-        hybrid = variant != "int8_convrot"
+        hybrid = variant.startswith("mxfp4")
         rot = variant == "mxfp4_rotated_hybrid"
+        fused = variant == "int8_convrot_fused_swiglu"
         rec(0)
         if hybrid:
             cr.mx_linear(x1, *mxw[rot][0], out=qkv, workspace=wsm, rotate=rot)
@@ -239,6 +362,13 @@ def hybrid_bench(torch, cr, dev, steps):
         rec(3)
         x3 = workloads.chain_outliers(o2, idx[2])
         rec(4)
+        if fused:
+            # fc1 with SwiGLU in its epilogue, then the down projection on h
+            cr.linear_swiglu(x3, *q8[2], out=h_, workspace=ws8)
+            rec(5)
+            cr.linear(h_, *q8[3], out=o4, workspace=ws8)
+            rec(6)
+            return
         if hybrid:
             cr.mx_linear(x3, *mxw[rot][1], out=gu_, workspace=wsm, rotate=rot)
         else:
@@ -253,7 +383,7 @@ def hybrid_bench(torch, cr, dev, steps):
            "projections_ms": {}}
     outs = {}
     n = max(3, min(steps, 10))
-    for name in ("int8_convrot", "mxfp4_hybrid", "mxfp4_rotated_hybrid"):
+    for name in ("int8_convrot", "int8_convrot_fused_swiglu", "mxfp4_hybrid", "mxfp4_rotated_hybrid"):
         run(name)
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(7)] for _ in range(n)]
         for i in range(n):
@@ -267,7 +397,8 @@ def hybrid_bench(torch, cr, dev, steps):
             "sum": round(float(med[0] + med[2] + med[4] + med[5]), 4)}
         run(name)
         torch.cuda.synchronize()
-        outs[name] = o4.float().clone()
+        if name != "int8_convrot_fused_swiglu":
+            outs[name] = o4.float().clone()
     a8 = res["projections_ms"]["int8_convrot"]
     ops = {"qkv": 2.0 * M * 3 * H * H, "ffn_input": 2.0 * M * 2 * F * H}
     res["change_pct"] = {}
@@ -276,6 +407,17 @@ def hybrid_bench(torch, cr, dev, steps):
         res["change_pct"][name] = {k: round(100.0 * (am[k] / a8[k] - 1.0), 1) for k in a8}
         res["tflops_" + name] = {k: round(ops[k] / (am[k] * 1e-3) / 1e12, 1) for k in ops}
     res["int8_tops"] = {k: round(ops[k] / (a8[k] * 1e-3) / 1e12, 1) for k in ops}
+    # the block chain with fc1's SwiGLU fused into its epilogue: per projection
+    # (each including its rotate+quantize pass) and the four together
+    fz = res["projections_ms"]["int8_convrot_fused_swiglu"]
+    ops4 = {"qkv": 2.0 * M * 3 * H * H, "attention_output": 2.0 * M * H * H,
+            "ffn_input": 2.0 * M * 2 * F * H, "ffn_output_swiglu": 2.0 * M * H * F}
+    ops4["sum"] = sum(ops4.values())
+    res["int8_fused_chain_tops"] = {k: round(ops4[k] / (fz[k] * 1e-3) / 1e12, 1) for k in ops4}
+    res["int8_fused_chain_pct_int8_peak"] = round(100.0 * ops4["sum"] / (fz["sum"] * 1e-3) / 1e12 / PEAK_INT8_TOPS, 1)
+    res["note_fused"] = ("int8_convrot_fused_swiglu: fc1 = convrot_linear_swiglu (SwiGLU in the GEMM epilogue), "
+                         "down = convrot_linear on h; its ffn_input includes SwiGLU and ffn_output_swiglu is the "
+                         "plain down projection")
     res["note_tflops"] = ("per projection call including its activation quantize pass; "
                           "dense MFMA peaks: fp4 10.1 PFLOP/s, int8 5.0 POP/s")
 
@@ -308,7 +450,7 @@ def hybrid_bench(torch, cr, dev, steps):
     res["finite"] = bool(all(torch.isfinite(o).all().item() for o in outs.values()))
     res["note"] = ("one synthetic block (random weights, attention replaced by the seeded mixing); "
                    "the pages' cosines are over 50 trained blocks on other hardware, context only")
-    del W, q8, mxw, ws8, wsm, qkv, o2, gu_, qh, sh, o4, outs, ref, x0, x1
+    del W, q8, mxw, ws8, wsm, qkv, o2, gu_, qh, sh, o4, h_, outs, ref, x0, x1
     torch.cuda.empty_cache()
     return res
 
@@ -608,6 +750,7 @@ def main():
     # the same shape for context.
     attention = attention_bench(torch, cr, dev, args.steps)
     hybrid = hybrid_bench(torch, cr, dev, args.steps)
+    qkv = qkv_bench(torch, cr, dev, args.steps)
 
     # cross-check: the same step through the fused entry points (same kernels)
     torch.cuda.synchronize()
@@ -624,13 +767,25 @@ def main():
     torch.cuda.synchronize()
     fused_ms = f0.elapsed_time(f1) / args.steps
 
+    # the clock the chip sustains under the dominant kernel (live, amd-smi)
+    clock = None
+    try:
+        clock = sustained_clock(torch, lambda: cr.gemm_swiglu(qx1, sx1, qwu, swu, out=h), ops_up)
+    except Exception as exc:   # reported as unavailable, not fatal
+        log("clock sampling failed: %s" % exc)
+
     d_up = kern["gemm_swiglu_up"]["ms"]
     roofline = {"kernel": "gemm_swiglu_up (int8 MFMA GEMM + SwiGLU epilogue)", "bound": "mfma",
                 "achieved": round(ops_up / (d_up * 1e-3) / 1e12, 1), "peak": PEAK_INT8_TOPS,
                 "unit": "TOP/s", "frac": round(ops_up / (d_up * 1e-3) / 1e12 / PEAK_INT8_TOPS, 4),
                 "traffic": measured_traffic("gemm_swiglu_up"),
                 "per_launch_ops": ops_up,
-                "per_launch_min_bytes": M * K1 + N1 * K1 + 2 * M * I + 4 * (M + N1)}
+                "per_launch_min_bytes": M * K1 + N1 * K1 + 2 * M * I + 4 * (M + N1),
+                "clock_ghz": clock["clock_ghz"] if clock else None,
+                "frac_at_measured_clock": (round(ops_up / (d_up * 1e-3) / 1e12 /
+                                                 (PEAK_INT8_TOPS * clock["clock_ghz"] / 2.4), 4) if clock else None),
+                "clock_note": "peak scaled by the measured clock / 2.4 GHz; clock sampled live by amd-smi while "
+                              "this kernel ran back to back (see sustained_clock)"}
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -665,6 +820,24 @@ def main():
                                       "load time; algorithmic bytes 18 n k + 4 r (n + k) + 8 n"},
         "attention_int8": attention,
         "mxfp4_hybrid": hybrid,
+        "qkv_projection": qkv,
+        "sustained_clock": clock,
+        "per_config": {
+            "cfg2_qkv_4096x5376x16128": {"gemm_TOPS": qkv["gemm_dequant"]["TOPS"],
+                                         "gemm_pct_int8_peak": qkv["gemm_dequant"]["pct_int8_peak"],
+                                         "end_to_end_TOPS": qkv["linear_end_to_end"]["TOPS"]},
+            "cfg3_ffn_up_swiglu": {"gemm_TOPS": kern["gemm_swiglu_up"]["TOPS"],
+                                   "gemm_pct_int8_peak": kern["gemm_swiglu_up"]["pct_int8_peak"],
+                                   "end_to_end_TOPS": round(ops_up / ((kern["rotate_quant_up"]["ms"] +
+                                                                       kern["gemm_swiglu_up"]["ms"]) * 1e-3) / 1e12, 1)},
+            "cfg4_ffn_down": {"gemm_TOPS": kern["gemm_dequant_down"]["TOPS"],
+                              "gemm_pct_int8_peak": kern["gemm_dequant_down"]["pct_int8_peak"],
+                              "end_to_end_TOPS": round(ops_dn / ((kern["rotate_quant_down"]["ms"] +
+                                                                  kern["gemm_dequant_down"]["ms"]) * 1e-3) / 1e12, 1)},
+            "cfg5_block_chain_fused": {"projections_ms": hybrid["projections_ms"]["int8_convrot_fused_swiglu"],
+                                       "TOPS": hybrid["int8_fused_chain_tops"],
+                                       "pct_int8_peak": hybrid["int8_fused_chain_pct_int8_peak"]},
+        },
         "wall_s": round(wall, 3),
     }
     print(json.dumps(out), flush=True)
