@@ -101,17 +101,31 @@ struct F32Rows {    // weights, fp32 [rows, k]
 // SwiGLU on fc1's bf16 output [rows, 2k] (hybrid model card, "Native NVFP4
 // projection benchmarks": an "FFN output + SwiGLU" projection): gate columns
 // [0, k), up columns [k, 2k), h = bf16(silu(g) * u), widened exactly; the
-// rotation then runs on h as on any bf16 activation row.
+// rotation then runs on h as on any bf16 activation row.  Each h is first
+// evaluated fast (swiglu_fast); only the elements whose fast value lies near
+// a bf16 rounding midpoint (or |g| > 16, or h huge) are evaluated again by
+// the definition (swiglu_f32), so every bf16 h is the definition's.
 struct SwiGluRows {
     const uint16_t* gu;
     __device__ __forceinline__ void load(int64_t row, int64_t k, int64_t off, float v[16]) const {
         const uint16_t* r = gu + row * 2 * k;
-        float g[16], u[16];
+        float g[16], u[16], h[16];
         load16(r + off, g);
         load16(r + k + off, u);
+        uint32_t redo = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            h[e] = swiglu_fast(g[e], u[e]);
+            redo |= swiglu_fast_ok(g[e], h[e]) ? 0u : 1u << e;
+        }
+        if (redo) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if (redo & (1u << e)) h[e] = swiglu_f32(g[e], u[e]);
+        }
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
-            const uint32_t b = pack_bf16(swiglu_f32(g[e], u[e]), swiglu_f32(g[e + 1], u[e + 1]));
+            const uint32_t b = pack_bf16(h[e], h[e + 1]);
             v[e] = __uint_as_float(b << 16);
             v[e + 1] = __uint_as_float(b & 0xffff0000u);
         }

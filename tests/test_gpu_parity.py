@@ -256,6 +256,43 @@ def test_swiglu_rotate_quant(cr, m, i):
         assert gu.host(sh)[0] == 0 and not gu.host(qh)[0].any()
 
 
+def test_swiglu_rotate_quant_near_bf16_midpoints(cr):
+    """h = bf16(silu(g) u) where the fp32 value lies within a few units in
+    the last place of a bf16 rounding midpoint, the cases where any evaluation
+    but the definition's could round h the other way.  Each row holds one
+    such (g, u) pair and zeros elsewhere, so the rotated row is +-h/16 at every
+    position and the row scale |h| / 16 / 127 pins h's bf16 value: scales and
+    codes must equal the oracle's bit for bit.  Pairs are picked from a seeded
+    pool by an fp64 estimate of h (the expected values are the oracle's);
+    |g| spans the fast range and beyond it."""
+    rng = np.random.default_rng(77)
+    n = 1 << 24
+    sig = rng.choice(np.array([0.3, 2.0, 6.0, 14.0, 40.0], dtype=np.float32), n)
+    g = oracle.bf16_to_f32(workloads.to_bf16_bits(rng.standard_normal(n, dtype=np.float32) * sig))
+    u = oracle.bf16_to_f32(workloads.to_bf16_bits(
+        rng.standard_normal(n, dtype=np.float32) * rng.choice(np.array([1e-3, 1.0, 300.0], dtype=np.float32), n)))
+    g64 = g.astype(np.float64)
+    h = (g64 / (1.0 + np.exp(-g64)) * u.astype(np.float64)).astype(np.float32)
+    low = h.view(np.uint32) & 0xFFFF
+    near = (np.abs(low.astype(np.int64) - 0x8000) <= 12) & (h != 0)
+    # for |g| > 16 silu(g) u is often the exact product g u, a bf16 tie; keep
+    # both sides of the fast range in the sample
+    small = np.nonzero(near & (np.abs(g) <= 16))[0][:4000]
+    large = np.nonzero(near & (np.abs(g) > 16))[0][:2000]
+    assert small.size > 1500 and large.size > 500, (small.size, large.size)
+    pick = np.concatenate([small, large])
+    m, i = pick.size, 256
+    gu_rows = np.zeros((m, 2 * i), dtype=np.float32)
+    cols = rng.integers(0, i, m)
+    gu_rows[np.arange(m), cols] = g[pick]
+    gu_rows[np.arange(m), i + cols] = u[pick]
+    gu_in = workloads.to_bf16_bits(gu_rows)
+    qh, sh = cr.swiglu_rotate_quant_act(gu.dev_bf16(gu_in))
+    oq, os_ = oracle.swiglu_rotate_quant_act(gu_in)
+    gu.assert_equal(_f32_bits(gu.host(sh)), _f32_bits(os_), "near-midpoint s_h (%d rows)" % m)
+    gu.assert_equal(gu.host(qh), oq, "near-midpoint q_h (%d rows)" % m)
+
+
 def test_output_side_swiglu_chain_small(cr):
     """The whole FFN with SwiGLU on fc1's output side, small: x -> fc1 (bf16
     dequant on 2i columns) -> SwiGLU + rotate + quantize -> down GEMM, against
