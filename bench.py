@@ -13,7 +13,7 @@ both GEMMs / step time), the roofline of the dominant kernel (the fused
 SwiGLU GEMM, against the dense int8 MFMA peak), and the CPU oracle timed on a
 bounded sample of the same step.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-clock]
 """
 from __future__ import annotations
 
@@ -461,6 +461,9 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true",
+                    help="skip the amd-smi clock sampling (for runs under a profiler, whose preloaded library "
+                         "would follow the amd-smi child process)")
     ap.add_argument("--m", type=int, default=None, help="token rows (default 32256)")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -769,10 +772,11 @@ def main():
 
     # the clock the chip sustains under the dominant kernel (live, amd-smi)
     clock = None
-    try:
-        clock = sustained_clock(torch, lambda: cr.gemm_swiglu(qx1, sx1, qwu, swu, out=h), ops_up)
-    except Exception as exc:   # reported as unavailable, not fatal
-        log("clock sampling failed: %s" % exc)
+    if not args.no_clock:
+        try:
+            clock = sustained_clock(torch, lambda: cr.gemm_swiglu(qx1, sx1, qwu, swu, out=h), ops_up)
+        except Exception as exc:   # reported as unavailable, not fatal
+            log("clock sampling failed: %s" % exc)
 
     d_up = kern["gemm_swiglu_up"]["ms"]
     roofline = {"kernel": "gemm_swiglu_up (int8 MFMA GEMM + SwiGLU epilogue)", "bound": "mfma",
