@@ -55,31 +55,41 @@ __device__ __forceinline__ float swiglu_f32(float g, float u) {
 }
 
 // The same h = silu(g) * u, fast, for the output-side pass: the exponential
-// and the reciprocal on the transcendental unit, with -log2(e) split into
-// C_HI (14 significant bits, so g * C_HI is exact for every bf16 g with
-// |g| <= 16) and C_LO ln 2, and 2^(g C_LO) taken to first order:
-//   a = exp2(g C_HI), e = a + a (g C_LO ln 2), h = (g * rcp(1 + e)) * u.
-// For |g| <= 16, with exp2 and rcp each within 2 ulps, e is within about
-// 2^-21 of the fixed exponential's value relatively, and h lies within 30
-// fp32 steps (units in the last place of its bit pattern) of swiglu_f32(g, u);
-// a CPU model with exp2 and rcp pushed 2 ulps off in either direction never
-// exceeds 8.  So whenever the low 16 bits of this h are more than
-// SWIGLU_FAST_MARGIN steps from 0x8000 (the bf16 rounding midpoint) and h is
-// finite and below 2^127, its bf16 rounding equals that of swiglu_f32(g, u)
-// bit for bit; elsewhere the caller evaluates swiglu_f32.
+// and the reciprocal on the transcendental unit.  -log2(e) is split into C_HI
+// (15 significant bits, so g * C_HI is exact for every bf16 g) and C_LO ln 2,
+// and 2^(g C_LO) is taken to first order (the dropped square term stays below
+// 1e-7 relatively wherever the exponential is finite):
+//   a = exp2(g C_HI), e = a + a (g C_LO ln 2),
+//   d = (1 + e) 2^-64 (one fma: 1 + exp(-g) rounded once, then scaled),
+//   h = ((g * rcp(d)) 2^-64) * u.
+// The 2^-64 keeps the reciprocal's result normal for every finite d, so the
+// quotient g / (1 + exp(-g)) comes out with full precision down to g = -88.5;
+// for bf16 g <= -89 exp2 overflows, d = inf and the quotient is -0, as in the
+// definition, whose exponential overflows there too.  With exp2 and rcp each
+// within 2 ulps, h lies within about 20 fp32 steps (units in the last place
+// of its bit pattern) of swiglu_f32(g, u); a CPU model over every finite bf16
+// g, with exp2 and rcp pushed 2 ulps off in either direction, never exceeds
+// 10.  So whenever the low 16 bits of this h are more than SWIGLU_FAST_MARGIN
+// steps from 0x8000 (the bf16 rounding midpoint) and h is finite and below
+// 2^127, its bf16 rounding equals that of swiglu_f32(g, u) bit for bit;
+// elsewhere (this includes |g| >= 2^64, where g * rcp(d) overflows) the caller
+// evaluates swiglu_f32.  Subnormal h needs no exception: fp32 subnormals are
+// kept, and both evaluations end in the same multiply by u of a normal (or
+// zero) quotient.
 constexpr float SWIGLU_C_HI = -0x1.7154p+0f;
 constexpr float SWIGLU_C_LO_LN2 = -0x1.480fb6p-18f;
 constexpr uint32_t SWIGLU_FAST_MARGIN = 32;
 __device__ __forceinline__ float swiglu_fast(float g, float u) {
     const float a = __builtin_amdgcn_exp2f(g * SWIGLU_C_HI);
     const float e = __builtin_fmaf(a, g * SWIGLU_C_LO_LN2, a);
-    return (g * __builtin_amdgcn_rcpf(1.0f + e)) * u;
+    const float d = __builtin_fmaf(e, 0x1p-64f, 0x1p-64f);
+    return ((g * __builtin_amdgcn_rcpf(d)) * 0x1p-64f) * u;
 }
-// true when the fast value h (from g) decides the bf16 rounding of swiglu_f32
-__device__ __forceinline__ bool swiglu_fast_ok(float g, float h) {
+// true when the fast value h decides the bf16 rounding of swiglu_f32
+__device__ __forceinline__ bool swiglu_fast_ok(float h) {
     const uint32_t low = __float_as_uint(h) & 0xFFFFu;
     const bool far = (low - (0x8000u - SWIGLU_FAST_MARGIN)) > 2u * SWIGLU_FAST_MARGIN;
-    return far && __builtin_fabsf(g) <= 16.0f && __builtin_fabsf(h) < 0x1p127f;
+    return far && __builtin_fabsf(h) < 0x1p127f;
 }
 
 }  // namespace convrot

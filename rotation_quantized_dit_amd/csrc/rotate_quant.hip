@@ -103,8 +103,8 @@ struct F32Rows {    // weights, fp32 [rows, k]
 // [0, k), up columns [k, 2k), h = bf16(silu(g) * u), widened exactly; the
 // rotation then runs on h as on any bf16 activation row.  Each h is first
 // evaluated fast (swiglu_fast); only the elements whose fast value lies near
-// a bf16 rounding midpoint (or |g| > 16, or h huge) are evaluated again by
-// the definition (swiglu_f32), so every bf16 h is the definition's.
+// a bf16 rounding midpoint (or is huge, infinite or NaN) are evaluated again
+// by the definition (swiglu_f32), so every bf16 h is the definition's.
 struct SwiGluRows {
     const uint16_t* gu;
     __device__ __forceinline__ void load(int64_t row, int64_t k, int64_t off, float v[16]) const {
@@ -116,7 +116,7 @@ struct SwiGluRows {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             h[e] = swiglu_fast(g[e], u[e]);
-            redo |= swiglu_fast_ok(g[e], h[e]) ? 0u : 1u << e;
+            redo |= swiglu_fast_ok(h[e]) ? 0u : 1u << e;
         }
         if (redo) {
 #pragma unroll

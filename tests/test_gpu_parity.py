@@ -264,28 +264,42 @@ def test_swiglu_rotate_quant_near_bf16_midpoints(cr):
     position and the row scale |h| / 16 / 127 pins h's bf16 value: scales and
     codes must equal the oracle's bit for bit.  Pairs are picked from a seeded
     pool by an fp64 estimate of h (the expected values are the oracle's);
-    |g| spans the fast range and beyond it."""
+    g spans both signs well past |g| = 16, down to -88.5, where the
+    exponential of -g is near the top of the fp32 range.  Further rows, not
+    picked near midpoints: g in [-120, -60] (for g <= -89 the definition's
+    exponential overflows and its quotient is -0), and |g| near 2^60..2^70,
+    where the fast quotient overflows and the definition is taken."""
     rng = np.random.default_rng(77)
     n = 1 << 24
-    sig = rng.choice(np.array([0.3, 2.0, 6.0, 14.0, 40.0], dtype=np.float32), n)
+    sig = rng.choice(np.array([0.3, 2.0, 6.0, 14.0, 40.0, 71.0], dtype=np.float32), n)
     g = oracle.bf16_to_f32(workloads.to_bf16_bits(rng.standard_normal(n, dtype=np.float32) * sig))
     u = oracle.bf16_to_f32(workloads.to_bf16_bits(
         rng.standard_normal(n, dtype=np.float32) * rng.choice(np.array([1e-3, 1.0, 300.0], dtype=np.float32), n)))
     g64 = g.astype(np.float64)
-    h = (g64 / (1.0 + np.exp(-g64)) * u.astype(np.float64)).astype(np.float32)
+    with np.errstate(over="ignore"):
+        h = (g64 / (1.0 + np.exp(-g64)) * u.astype(np.float64)).astype(np.float32)
     low = h.view(np.uint32) & 0xFFFF
     near = (np.abs(low.astype(np.int64) - 0x8000) <= 12) & (h != 0)
-    # for |g| > 16 silu(g) u is often the exact product g u, a bf16 tie; keep
-    # both sides of the fast range in the sample
+    # for g > 16 silu(g) u is often the exact product g u, a bf16 tie; keep
+    # every range in the sample
     small = np.nonzero(near & (np.abs(g) <= 16))[0][:4000]
-    large = np.nonzero(near & (np.abs(g) > 16))[0][:2000]
-    assert small.size > 1500 and large.size > 500, (small.size, large.size)
-    pick = np.concatenate([small, large])
-    m, i = pick.size, 256
+    pos = np.nonzero(near & (g > 16))[0][:1000]
+    neg = np.nonzero(near & (g < -16))[0][:1000]
+    assert small.size > 1500 and pos.size > 300 and neg.size > 300, (small.size, pos.size, neg.size)
+    pick = np.concatenate([small, pos, neg])
+    g_pick, u_pick = g[pick], u[pick]
+    tail_g = oracle.bf16_to_f32(workloads.to_bf16_bits(rng.uniform(-120.0, -60.0, 1000).astype(np.float32)))
+    tail_u = oracle.bf16_to_f32(workloads.to_bf16_bits(rng.standard_normal(1000, dtype=np.float32)))
+    huge_g = oracle.bf16_to_f32(workloads.to_bf16_bits(
+        (rng.choice([-1.0, 1.0], 100) * np.exp2(rng.uniform(60.0, 70.0, 100))).astype(np.float32)))
+    huge_u = oracle.bf16_to_f32(workloads.to_bf16_bits((1e-3 * rng.standard_normal(100)).astype(np.float32)))
+    g_pick = np.concatenate([g_pick, tail_g, huge_g])
+    u_pick = np.concatenate([u_pick, tail_u, huge_u])
+    m, i = g_pick.size, 256
     gu_rows = np.zeros((m, 2 * i), dtype=np.float32)
     cols = rng.integers(0, i, m)
-    gu_rows[np.arange(m), cols] = g[pick]
-    gu_rows[np.arange(m), i + cols] = u[pick]
+    gu_rows[np.arange(m), cols] = g_pick
+    gu_rows[np.arange(m), i + cols] = u_pick
     gu_in = workloads.to_bf16_bits(gu_rows)
     qh, sh = cr.swiglu_rotate_quant_act(gu.dev_bf16(gu_in))
     oq, os_ = oracle.swiglu_rotate_quant_act(gu_in)
