@@ -58,11 +58,16 @@ typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 
 // Streaming loads: each input byte is read once, so they bypass cache reuse.
-__device__ __forceinline__ void load16(const uint16_t* __restrict__ p, float v[16]) {
+struct Bf16x16 {    // 16 raw bf16 values
+    v4u a, b;
+};
+__device__ __forceinline__ Bf16x16 fetch16(const uint16_t* __restrict__ p) {
     const v4u* q = reinterpret_cast<const v4u*>(p);
-    v4u a = __builtin_nontemporal_load(q);
-    v4u b = __builtin_nontemporal_load(q + 1);
-    uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+    return Bf16x16{__builtin_nontemporal_load(q), __builtin_nontemporal_load(q + 1)};
+}
+// bf16 -> fp32 is exact: the bits move to the top half.
+__device__ __forceinline__ void widen16(const Bf16x16& r, float v[16]) {
+    const uint32_t w[8] = {r.a.x, r.a.y, r.a.z, r.a.w, r.b.x, r.b.y, r.b.z, r.b.w};
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         v[2 * i] = __uint_as_float(w[i] << 16);
@@ -70,31 +75,40 @@ __device__ __forceinline__ void load16(const uint16_t* __restrict__ p, float v[1
     }
 }
 
-__device__ __forceinline__ void load16(const float* __restrict__ p, float v[16]) {
-    const v4f* q = reinterpret_cast<const v4f*>(p);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        v4f t = __builtin_nontemporal_load(q + i);
-        v[4 * i] = t.x;
-        v[4 * i + 1] = t.y;
-        v[4 * i + 2] = t.z;
-        v[4 * i + 3] = t.w;
-    }
-}
-
 // Input sources: how a lane obtains the 16 fp32 values at element offset
-// off (a multiple of 16) of row `row` of a k-wide input.
+// off (a multiple of 16) of row `row` of a k-wide input, in two steps: fetch
+// issues the loads into a Raw register block, expand turns it into values.
+// The rows kernel fetches every pass of a lane before expanding any, so all
+// of a lane's loads are in flight together even when expand branches.
 struct Bf16Rows {   // activations, bf16 [rows, k]
     const uint16_t* x;
-    __device__ __forceinline__ void load(int64_t row, int64_t k, int64_t off, float v[16]) const {
-        load16(x + row * k + off, v);
+    typedef Bf16x16 Raw;
+    __device__ __forceinline__ Raw fetch(int64_t row, int64_t k, int64_t off) const {
+        return fetch16(x + row * k + off);
     }
+    __device__ __forceinline__ void expand(const Raw& r, float v[16]) const { widen16(r, v); }
 };
 
 struct F32Rows {    // weights, fp32 [rows, k]
     const float* x;
-    __device__ __forceinline__ void load(int64_t row, int64_t k, int64_t off, float v[16]) const {
-        load16(x + row * k + off, v);
+    struct Raw {
+        v4f t[4];
+    };
+    __device__ __forceinline__ Raw fetch(int64_t row, int64_t k, int64_t off) const {
+        const v4f* q = reinterpret_cast<const v4f*>(x + row * k + off);
+        Raw r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) r.t[i] = __builtin_nontemporal_load(q + i);
+        return r;
+    }
+    __device__ __forceinline__ void expand(const Raw& r, float v[16]) const {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[4 * i] = r.t[i].x;
+            v[4 * i + 1] = r.t[i].y;
+            v[4 * i + 2] = r.t[i].z;
+            v[4 * i + 3] = r.t[i].w;
+        }
     }
 };
 
@@ -107,22 +121,30 @@ struct F32Rows {    // weights, fp32 [rows, k]
 // by the definition (swiglu_f32), so every bf16 h is the definition's.
 struct SwiGluRows {
     const uint16_t* gu;
-    __device__ __forceinline__ void load(int64_t row, int64_t k, int64_t off, float v[16]) const {
+    struct Raw {
+        Bf16x16 g, u;
+    };
+    __device__ __forceinline__ Raw fetch(int64_t row, int64_t k, int64_t off) const {
         const uint16_t* r = gu + row * 2 * k;
+        return Raw{fetch16(r + off), fetch16(r + k + off)};
+    }
+    __device__ __forceinline__ void expand(const Raw& r, float v[16]) const {
         float g[16], u[16], h[16];
-        load16(r + off, g);
-        load16(r + k + off, u);
-        uint32_t redo = 0;
+        widen16(r.g, g);
+        widen16(r.u, u);
+        // Each element's check is a lane mask; the definition runs under
+        // it, element by element.  (Collecting the checks into a per-lane
+        // bit mask first held 16 more registers and cost a workgroup per
+        // CU.)
+        bool ok[16];
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             h[e] = swiglu_fast(g[e], u[e]);
-            redo |= swiglu_fast_ok(h[e]) ? 0u : 1u << e;
+            ok[e] = swiglu_fast_ok(h[e]);
         }
-        if (redo) {
 #pragma unroll
-            for (int e = 0; e < 16; ++e)
-                if (redo & (1u << e)) h[e] = swiglu_f32(g[e], u[e]);
-        }
+        for (int e = 0; e < 16; ++e)
+            if (!ok[e]) h[e] = swiglu_f32(g[e], u[e]);
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
             const uint32_t b = pack_bf16(h[e], h[e + 1]);
@@ -202,12 +224,18 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_rows_kernel(
     int8_t* qr = q + row * k;
     float* tile = smem + wave * kWaveFloats + sub * kTile;
 
+    typename Src::Raw raw[P];
+#pragma unroll
+    for (int p = 0; p < P; ++p) {
+        const int g = (p * W + wave) * 4 + sub;
+        if (g < G) raw[p] = src.fetch(row, k, (int64_t)g * 256 + j * 16);
+    }
     float vals[P][16];
 #pragma unroll
     for (int p = 0; p < P; ++p) {
         const int g = (p * W + wave) * 4 + sub;
         if (g < G) {
-            src.load(row, k, (int64_t)g * 256 + j * 16, vals[p]);
+            src.expand(raw[p], vals[p]);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) vals[p][i] = 0.0f;
@@ -263,7 +291,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_long_kernel(
         const int g = (p * W + wave) * 4 + sub;
         float t[16];
         if (g < G) {
-            src.load(row, k, (int64_t)g * 256 + j * 16, t);
+            src.expand(src.fetch(row, k, (int64_t)g * 256 + j * 16), t);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) t[i] = 0.0f;
@@ -289,7 +317,7 @@ __global__ __launch_bounds__(kMaxWaves * 64) void rotate_quant_long_kernel(
         const int g = (p * W + wave) * 4 + sub;
         float t[16];
         if (g < G) {
-            src.load(row, k, (int64_t)g * 256 + j * 16, t);
+            src.expand(src.fetch(row, k, (int64_t)g * 256 + j * 16), t);
         } else {
 #pragma unroll
             for (int i = 0; i < 16; ++i) t[i] = 0.0f;
