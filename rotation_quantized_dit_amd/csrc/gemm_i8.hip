@@ -98,9 +98,10 @@ constexpr int COPIES = MA + 2;
 // copies of a refill issued in the k-step after the stage barrier; the rest
 // go out in the next stage's first k-step
 constexpr int COPIES_NOW = 3;
-// Epilogue staging: each wave parks 32 rows x 128 int32 at a time, rows
-// padded to PITCH int32 to spread banks; it reuses the ring's memory, and
-// the tile's row scales follow it.
+// Epilogue staging: each wave parks 32 rows of its outputs at a time in the
+// ring's memory (bf16 outputs as bf16; the int32 output as int32, rows
+// padded to PITCH int32 to spread banks), and the tile's row scales follow
+// the largest of those areas.
 constexpr int PITCH = 136;
 constexpr int STASH_WAVE_BYTES = 32 * PITCH * 4;
 constexpr int STASH_BYTES = NWAVES * STASH_WAVE_BYTES;
@@ -112,6 +113,7 @@ static_assert(STAGES * COPIES < 64, "vmcnt range");
 
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v16i __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
@@ -411,19 +413,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
 
     // Epilogue.  Block (a, b), lane l, register r of the MFMA accumulators
     // holds row 32 a + 8 (r / 4) + 4 (l / 32) + r % 4 and column 32 b + l % 32
-    // of the wave's 96 x 128 sub-tile.  Row block by row block, each wave
-    // parks its 32 x 128 int32 accumulators in its own part of the (now free)
-    // ring, then reads them back row-contiguous: every lane takes 8
-    // consecutive columns of one row, applies the scales and the epilogue math
-    // in a compact loop, and writes one 16-byte store.
-    // s_w of the lane's 8 output columns (gate and up columns for SwiGLU)
-    float swa[8], swb[8];
+    // of the wave's 96 x 128 sub-tile.  For bf16 outputs each lane forms its
+    // values where they lie (dequant, and for SwiGLU silu(g) u from the gate
+    // block b and the up block b + 2 of the same outputs) and parks them as
+    // bf16 in its wave's part of the (now free) ring, 32 rows at a time;
+    // the rows are then read back contiguous, 16 bytes per lane, and leave
+    // as one 16-byte store.  The int32 output parks the accumulators
+    // themselves.
+    const int l31 = lane & 31, hl = lane >> 5;
+    // s_w of the lane's accumulator columns: b = 0..3 (BF16), or the gate
+    // (b = 0, 1) and up (b = 2, 3) rows of h column 32 (b & 1) + l % 32
+    float swv[4];
     if constexpr (EP != Epilogue::S32) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int c = (epi_col0 + e) < N ? (epi_col0 + e) : (N - 1);
-            swa[e] = sw[c];
-            swb[e] = EP == Epilogue::SWIGLU ? sw[N + c] : 0.0f;
+        for (int bb = 0; bb < 4; ++bb) {
+            int c;
+            if constexpr (EP == Epilogue::SWIGLU)
+                c = tile.tn * (BN / 2) + 64 * wn + 32 * (bb & 1) + l31;
+            else
+                c = tile.tn * BN + 128 * wn + 32 * bb + l31;
+            c = c < N ? c : N - 1;
+            swv[bb] = sw[(EP == Epilogue::SWIGLU && bb >= 2 ? N : 0) + c];
         }
     }
     lds_barrier();   // every wave is done reading the ring
@@ -432,68 +442,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         if (tid < BM) sx_lds[tid] = sx_own;
         lds_barrier();
     }
-    int32_t* stash = reinterpret_cast<int32_t*>(lds + wave * STASH_WAVE_BYTES);
     const int grow0 = m0 + 32 * MA * wm;
-
-    auto stash_block = [&](int a) {
-        asm volatile("" ::: "memory");
-#pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                stash[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * PITCH + 32 * b + (lane & 31)] =
-                    acc[a][b][r];
-        asm volatile("" ::: "memory");
-    };
-
     const int col0 = epi_col0;
     const int cg = epi_cg;
     const int ro = epi_ro;
     const bool vec_cols = (col0 + 8 <= N) && (N % 8 == 0);
-    if constexpr (EP == Epilogue::SWIGLU) {
-        // lane -> 8 output columns (gate j, up i + j) and a row phase of 8
-        uint16_t* y = reinterpret_cast<uint16_t*>(out);
+
+    if constexpr (EP == Epilogue::S32) {
+        int32_t* stash = reinterpret_cast<int32_t*>(lds + wave * STASH_WAVE_BYTES);
+        int32_t* o = reinterpret_cast<int32_t*>(out);
 #pragma unroll
         for (int a = 0; a < MA; ++a) {
-            stash_block(a);
-#pragma nounroll
-            for (int it = 0; it < 4; ++it) {
-                const int lr = 8 * it + ro;
-                const int grow = grow0 + 32 * a + lr;
-                const float sxr = sx_lds[32 * MA * wm + 32 * a + lr];
-                const v4i g0 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg);
-                const v4i g1 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg + 4);
-                const v4i u0 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 64 + 8 * cg);
-                const v4i u1 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 64 + 8 * cg + 4);
-                const int ga[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
-                const int ua[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
-                float h[8];
+            asm volatile("" ::: "memory");
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const float g = dequant(ga[e], sxr, swa[e]);
-                    const float u = dequant(ua[e], sxr, swb[e]);
-                    h[e] = swiglu_hw(g, u);
-                }
-                const v4u pk = {pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]), pack_bf16(h[4], h[5]),
-                                pack_bf16(h[6], h[7])};
-                if (grow < M) {
-                    if (vec_cols) {
-                        *reinterpret_cast<v4u*>(y + (int64_t)grow * N + col0) = pk;
-                    } else {
-                        const uint32_t pw[4] = {pk.x, pk.y, pk.z, pk.w};
+            for (int bb = 0; bb < 4; ++bb)
 #pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (col0 + e < N)
-                                y[(int64_t)grow * N + col0 + e] = (uint16_t)(pw[e >> 1] >> (16 * (e & 1)));
-                    }
-                }
-            }
-        }
-    } else {
-        // lane -> 8 output columns and a row phase of 4
-#pragma unroll
-        for (int a = 0; a < MA; ++a) {
-            stash_block(a);
+                for (int r = 0; r < 16; ++r)
+                    stash[(8 * (r >> 2) + 4 * hl + (r & 3)) * PITCH + 32 * bb + l31] = acc[a][bb][r];
+            asm volatile("" ::: "memory");
 #pragma nounroll
             for (int it = 0; it < 8; ++it) {
                 const int lr = 4 * it + ro;
@@ -501,26 +467,65 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                 const v4i a0 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg);
                 const v4i a1 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg + 4);
                 if (grow >= M) continue;
-                if constexpr (EP == Epilogue::S32) {
-                    int32_t* o = reinterpret_cast<int32_t*>(out);
-                    if (vec_cols) {
-                        *reinterpret_cast<v4i*>(o + (int64_t)grow * N + col0) = a0;
-                        *reinterpret_cast<v4i*>(o + (int64_t)grow * N + col0 + 4) = a1;
-                    } else {
-                        const int av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-#pragma unroll
-                        for (int e = 0; e < 8; ++e)
-                            if (col0 + e < N) o[(int64_t)grow * N + col0 + e] = av[e];
-                    }
+                if (vec_cols) {
+                    *reinterpret_cast<v4i*>(o + (int64_t)grow * N + col0) = a0;
+                    *reinterpret_cast<v4i*>(o + (int64_t)grow * N + col0 + 4) = a1;
                 } else {
-                    uint16_t* y = reinterpret_cast<uint16_t*>(out);
-                    const float sxr = sx_lds[32 * MA * wm + 32 * a + lr];
                     const int av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-                    float h[8];
 #pragma unroll
-                    for (int e = 0; e < 8; ++e) h[e] = dequant(av[e], sxr, swa[e]);
-                    const v4u pk = {pack_bf16(h[0], h[1]), pack_bf16(h[2], h[3]), pack_bf16(h[4], h[5]),
-                                    pack_bf16(h[6], h[7])};
+                    for (int e = 0; e < 8; ++e)
+                        if (col0 + e < N) o[(int64_t)grow * N + col0 + e] = av[e];
+                }
+            }
+        }
+    } else {
+        // bf16 rows of 64 (SwiGLU) or 128 outputs, padded to P16 bf16 so that
+        // the two lane halves (rows r and r + 4) write disjoint banks
+        constexpr int NB = EP == Epilogue::SWIGLU ? 2 : 4;     // output blocks per wave row
+        constexpr int P16 = 32 * NB + 8;
+        constexpr int ITS = EP == Epilogue::SWIGLU ? 4 : 8;    // read-back rows per lane
+        constexpr int ROW_STEP = 32 / ITS;
+        uint16_t* st16 = reinterpret_cast<uint16_t*>(lds + wave * (32 * P16 * 2));
+        uint16_t* y = reinterpret_cast<uint16_t*>(out);
+#pragma unroll
+        for (int a = 0; a < MA; ++a) {
+            // row scales of the lane's 16 rows: 32 a + 8 q + 4 (l / 32) + p
+            float sxr[16];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const v4f t4 = *reinterpret_cast<const v4f*>(sx_lds + 32 * MA * wm + 32 * a + 8 * q + 4 * hl);
+                sxr[4 * q] = t4.x;
+                sxr[4 * q + 1] = t4.y;
+                sxr[4 * q + 2] = t4.z;
+                sxr[4 * q + 3] = t4.w;
+            }
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int bb = 0; bb < NB; ++bb)
+#pragma unroll
+                for (int r = 0; r < 16; r += 2) {
+                    float v0, v1;
+                    if constexpr (EP == Epilogue::SWIGLU) {
+                        v0 = swiglu_hw(dequant(acc[a][bb][r], sxr[r], swv[bb]),
+                                       dequant(acc[a][bb + 2][r], sxr[r], swv[bb + 2]));
+                        v1 = swiglu_hw(dequant(acc[a][bb][r + 1], sxr[r + 1], swv[bb]),
+                                       dequant(acc[a][bb + 2][r + 1], sxr[r + 1], swv[bb + 2]));
+                    } else {
+                        v0 = dequant(acc[a][bb][r], sxr[r], swv[bb]);
+                        v1 = dequant(acc[a][bb][r + 1], sxr[r + 1], swv[bb]);
+                    }
+                    const uint32_t pk = pack_bf16(v0, v1);
+                    const int row = 8 * (r >> 2) + 4 * hl + (r & 3);   // rows row, row + 1
+                    st16[row * P16 + 32 * bb + l31] = (uint16_t)pk;
+                    st16[(row + 1) * P16 + 32 * bb + l31] = (uint16_t)(pk >> 16);
+                }
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int it = 0; it < ITS; ++it) {
+                const int lr = ROW_STEP * it + ro;
+                const int grow = grow0 + 32 * a + lr;
+                const v4u pk = *reinterpret_cast<const v4u*>(st16 + lr * P16 + 8 * cg);
+                if (grow < M) {
                     if (vec_cols) {
                         *reinterpret_cast<v4u*>(y + (int64_t)grow * N + col0) = pk;
                     } else {

@@ -67,11 +67,11 @@ constexpr int STAGE_BYTES = A_STAGE + B_STAGE + SA_BYTES + SB_BYTES;
 constexpr int STAGES = 3;
 constexpr int COPIES = MA + 3;               // per wave per stage: A, B and one scale copy
 constexpr int SPARE = STAGES * STAGE_BYTES;  // 1 KiB that the idle scale copies fill
-constexpr int PITCH = 136;
-constexpr int STASH_WAVE_BYTES = 32 * PITCH * 4;
-constexpr int STASH_BYTES = NWAVES * STASH_WAVE_BYTES;
+// epilogue: each wave parks 32 rows x 128 bf16 at a time, rows padded to P16
+constexpr int P16 = 136;
+constexpr int STASH_BYTES = NWAVES * 32 * P16 * 2;
 constexpr int RING_BYTES = STAGES * STAGE_BYTES;
-constexpr int LDS_BYTES = RING_BYTES > STASH_BYTES ? RING_BYTES : STASH_BYTES;
+constexpr int LDS_BYTES = RING_BYTES + 1024 > STASH_BYTES ? RING_BYTES + 1024 : STASH_BYTES;   // ring + spare
 constexpr int GROUP_M = 4;                   // M-tiles per raster group
 static_assert(SPARE + 1024 <= LDS_BYTES, "spare area");
 static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
@@ -311,30 +311,39 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
     if (kt + 1 < KT) stage(std::integral_constant<int, 1>{}, kt + 1);
     wait_vmcnt<0>();
 
+    // Epilogue.  Lane l, register r of accumulator block (a, b) holds row
+    // 32 a + 8 (r / 4) + 4 (l / 32) + r % 4 and column 32 b + l % 32 of the
+    // wave's 96 x 128 sub-tile.  Each lane rounds its values to bf16 where
+    // they lie and parks them in its wave's part of the (now free) ring, 32
+    // rows at a time, rows padded to P16 bf16 so that the two lane halves
+    // (rows r and r + 4) write disjoint banks; the rows are then read back
+    // contiguous, 16 bytes per lane, and leave as one 16-byte store.
     lds_barrier();
-    float* stash = reinterpret_cast<float*>(lds + wave * STASH_WAVE_BYTES);
+    uint16_t* st16 = reinterpret_cast<uint16_t*>(lds + wave * (32 * P16 * 2));
     const int grow0 = m0 + 32 * MA * wm;
     const int cg = lane % 16, ro = lane / 16;
     const int col0 = n0 + 128 * wn + 8 * cg;
     const bool vec_cols = (col0 + 8 <= N) && (N % 8 == 0);
+    const int l31 = lane & 31, hl = lane >> 5;
 #pragma unroll
     for (int a = 0; a < MA; ++a) {
         asm volatile("" ::: "memory");
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; ++r)
-                stash[(8 * (r >> 2) + 4 * (lane >> 5) + (r & 3)) * PITCH + 32 * b + (lane & 31)] = acc[a][b][r];
+            for (int r = 0; r < 16; r += 2) {
+                const uint32_t pk = pack_bf16(acc[a][b][r], acc[a][b][r + 1]);
+                const int row = 8 * (r >> 2) + 4 * hl + (r & 3);   // rows row, row + 1
+                st16[row * P16 + 32 * b + l31] = (uint16_t)pk;
+                st16[(row + 1) * P16 + 32 * b + l31] = (uint16_t)(pk >> 16);
+            }
         asm volatile("" ::: "memory");
-#pragma nounroll
+#pragma unroll
         for (int it = 0; it < 8; ++it) {
             const int lr = 4 * it + ro;
             const int grow = grow0 + 32 * a + lr;
-            const v4f a0 = *reinterpret_cast<const v4f*>(stash + lr * PITCH + 8 * cg);
-            const v4f a1 = *reinterpret_cast<const v4f*>(stash + lr * PITCH + 8 * cg + 4);
+            const v4u pk = *reinterpret_cast<const v4u*>(st16 + lr * P16 + 8 * cg);
             if (grow >= M) continue;
-            const v4u pk = {pack_bf16(a0.x, a0.y), pack_bf16(a0.z, a0.w), pack_bf16(a1.x, a1.y),
-                            pack_bf16(a1.z, a1.w)};
             if (vec_cols) {
                 *reinterpret_cast<v4u*>(out + (int64_t)grow * N + col0) = pk;
             } else {
