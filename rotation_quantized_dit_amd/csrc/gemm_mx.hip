@@ -25,7 +25,8 @@
 // assembly (so the compiler does not drain them before every fragment read),
 // a fixed MFMA order with each fragment register (and its block scale)
 // refilled right after its last use, the stage barrier after the fourth MFMA
-// of the second k-step, the refill copies spread over that k-step, copies
+// of the second k-step, four of the six refill copies spread over that
+// k-step and the other two in the next stage's first k-step, copies
 // past the last stage pushed out of the buffer's range, and the stage loop
 // unrolled over the ring's three slots so that every LDS offset is an
 // immediate (without that the slot arithmetic needs registers the loop does
@@ -260,14 +261,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
             fa_(2);
         }
     };
-    constexpr int CS[COPIES] = {4, 5, 6, 7, 8, 9};
+    // copies 0-3 of a refill go out after slots CS[] of the k-step that
+    // follows the barrier, copies 4 and 5 after slots 0 and 6 of the next
+    // stage's first k-step (before the first refill: stage STAGES - 1
+    // again, the same bytes into its slot)
+    constexpr int COPIES_NOW = 4;
+    constexpr int CS[COPIES_NOW] = {4, 6, 8, 10};
     constexpr int BARRIER_AFTER = 3;
     // One stage with its ring slot known at compile time (every LDS offset an
     // immediate); the stage loop runs in rounds of STAGES.
     auto stage = [&](auto slot_c, int kt) {
         constexpr int slot = decltype(slot_c)::value;
         constexpr int next = slot + 1 == STAGES ? 0 : slot + 1;
+        constexpr int prev_slot = slot == 0 ? STAGES - 1 : slot - 1;
         const uint32_t oob = kt + STAGES < KT ? 0u : OOB;
+        const int prev_kt = kt > 0 ? kt - 1 + STAGES : STAGES - 1;
+        const uint32_t prev_oob = prev_kt < KT ? 0u : OOB;
         const uint8_t* cur = lds + slot * STAGE_BYTES;
         const uint8_t* nxt = lds + next * STAGE_BYTES;
 #pragma unroll
@@ -275,6 +284,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
             __builtin_amdgcn_sched_barrier(0);
             mfma(i, 0);
             refill(i, cur, 1);
+            if (i == 0) issue(COPIES_NOW, prev_kt, prev_oob, prev_slot);
+            if (i == 6) issue(COPIES_NOW + 1, prev_kt, prev_oob, prev_slot);
         }
 #pragma unroll
         for (int i = 0; i <= BARRIER_AFTER; ++i) {
@@ -295,7 +306,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
                 refill(i, nxt, 0);
             }
 #pragma unroll
-            for (int j = 0; j < COPIES; ++j)
+            for (int j = 0; j < COPIES_NOW; ++j)
                 if (CS[j] == i) issue(j, kt + STAGES, oob, slot);
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -309,6 +320,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
     }
     if (kt < KT) stage(std::integral_constant<int, 0>{}, kt);
     if (kt + 1 < KT) stage(std::integral_constant<int, 1>{}, kt + 1);
+    // the deferred copies of the last refill (out of range)
+    issue(COPIES_NOW, KT - 1 + STAGES, OOB, (KT - 1) % STAGES);
+    issue(COPIES_NOW + 1, KT - 1 + STAGES, OOB, (KT - 1) % STAGES);
     wait_vmcnt<0>();
 
     // Epilogue.  Lane l, register r of accumulator block (a, b) holds row
