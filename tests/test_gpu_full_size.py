@@ -176,10 +176,15 @@ def _oracle_chain(ch, rows, qws, sws, gpu_ffn_up):
     x2 = workloads.chain_outliers(a, idx[1]).view(torch.int16).numpy().view(np.uint16)
     o2 = oracle.linear_rows(x2, qws[1], sws[1])
     x3 = workloads.chain_outliers(torch.from_numpy(o2.view(np.int16)).view(torch.bfloat16), idx[2])
-    ref3, mag3 = oracle.linear_swiglu_ref_rows(x3.view(torch.int16).numpy().view(np.uint16), qws[2], sws[2])
+    x3_bits = x3.view(torch.int16).numpy().view(np.uint16)
+    ref3, mag3 = oracle.linear_swiglu_ref_rows(x3_bits, qws[2], sws[2])
+    # the output-side placement: fc1 on all 2I columns in bf16, then SwiGLU + rotate + quantize
+    gu3 = oracle.linear_rows(x3_bits, qws[2], sws[2])
+    q_h, s_h = oracle.swiglu_rotate_quant_act(gu3)
     x4 = workloads.chain_outliers(torch.from_numpy(gpu_ffn_up.view(np.int16)).view(torch.bfloat16), idx[3])
     o4 = oracle.linear_rows(x4.view(torch.int16).numpy().view(np.uint16), qws[3], sws[3])
-    return {"qkv": qkv[[pos[r] for r in rows]], "attn_out": o2, "ffn_up": (ref3, mag3), "ffn_down": o4}
+    return {"qkv": qkv[[pos[r] for r in rows]], "attn_out": o2, "ffn_up": (ref3, mag3), "ffn_down": o4,
+            "gu3": gu3, "q_h": q_h, "s_h": s_h}
 
 
 @pytest.fixture(scope="module")
@@ -205,14 +210,18 @@ def block_chain(cr):
     o2 = cr.linear(x2, gq[1], gs[1])
     x3 = workloads.chain_outliers(o2, idx[2])
     o3 = cr.linear_swiglu(x3, gq[2], gs[2])
+    gu3 = cr.linear(x3, gq[2], gs[2])                  # output-side placement: bf16 gate/up, then the pass
+    qh3, sh3 = cr.swiglu_rotate_quant_act(gu3)
+    del gu3
     x4 = workloads.chain_outliers(o3, idx[3])
     o4 = cr.linear(x4, gq[3], gs[3])
     ridx = torch.from_numpy(rows).cuda()
     g = {"qkv": gu.host_bf16(qkv[ridx]), "attn_out": gu.host_bf16(o2[ridx]),
          "ffn_up": gu.host_bf16(o3[ridx]), "ffn_down": gu.host_bf16(o4[ridx]),
+         "q_h": gu.host(qh3[ridx]), "s_h": gu.host(sh3[ridx]),
          "q_w": [gu.host(q) for q in gq], "s_w": [gu.host(s) for s in gs],
          "finite": bool(torch.isfinite(o4.float()).all().item())}
-    del qkv, v, a, x2, o2, x3, o3, x4, o4, gq, gs
+    del qkv, v, a, x2, o2, x3, o3, x4, o4, gq, gs, qh3, sh3
     torch.cuda.synchronize()
     print("block chain: oracle", flush=True)
     qws, sws = zip(*[oracle.quantize_weight(w) for w in ch["w"]])
@@ -236,6 +245,22 @@ def test_block_chain_layer(block_chain, layer):
         gu.assert_swiglu_bound(g[layer], *o[layer], what)
     else:
         gu.assert_bf16_parity(g[layer], o[layer], what)
+
+
+def test_block_chain_output_side_swiglu(block_chain):
+    """The chain's FFN with SwiGLU on fc1's output side: fc1 on all 2I columns
+    in bf16, then SwiGLU + rotate + quantize, at full size.  The chain has no
+    normalization layers, so its gates spread widely (standard deviation near
+    70): the sampled rows reach the region g <= -89, where the definition's
+    exponential overflows and its quotient is -0, and the band (-88.5, -64]
+    where the fast evaluation scales its reciprocal.  Codes and scales must
+    equal the oracle's bit for bit."""
+    g, o, rows = block_chain
+    i = o["gu3"].shape[1] // 2
+    gates = oracle.bf16_to_f32(o["gu3"][:, :i])
+    assert np.any(gates <= -89.0) and np.any((gates > -88.5) & (gates <= -64.0)), "gate range not reached"
+    gu.assert_equal(_f32_bits(g["s_h"]), _f32_bits(o["s_h"]), "chain output-side SwiGLU s_h (sampled rows)")
+    gu.assert_equal(g["q_h"], o["q_h"], "chain output-side SwiGLU q_h (sampled rows)")
 
 
 def test_block_chain_finite_and_tail_rows(block_chain):
