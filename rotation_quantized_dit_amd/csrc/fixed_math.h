@@ -91,5 +91,16 @@ __device__ __forceinline__ bool swiglu_fast_ok(float h) {
     const bool far = (low - (0x8000u - SWIGLU_FAST_MARGIN)) > 2u * SWIGLU_FAST_MARGIN;
     return far && __builtin_fabsf(h) < 0x1p127f;
 }
+// true when the fast value is the definition's h exactly, wherever it lies:
+// for bf16 g in [16.75, 2^64), exp(-g) is below 2^-24 (at 16.625, the bf16
+// gate below, it is 1 % above), so the definition's 1 + exp(-g) rounds to 1
+// and its quotient is g.  The fast e, a few ulps from exp(-g), leaves
+// d = 2^-64 exactly there; the reciprocal of a power of two is exact (2^64),
+// g 2^64 2^-64 = g below 2^64, and both evaluations round the same product
+// g u.  Such products of two bf16 values are often exact bf16 ties, which
+// swiglu_fast_ok turns away.
+__device__ __forceinline__ bool swiglu_fast_exact(float g) {
+    return g >= 16.75f && g < 0x1p64f;
+}
 
 }  // namespace convrot

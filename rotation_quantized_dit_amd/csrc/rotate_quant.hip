@@ -144,7 +144,13 @@ struct SwiGluRows {
         }
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-            if (!ok[e]) h[e] = swiglu_f32(g[e], u[e]);
+            if (!ok[e]) {
+                // The empty asm keeps this test inside the rare branch, not
+                // hoisted into every element's path.
+                float gk = g[e];
+                asm volatile("" : "+v"(gk));
+                if (!swiglu_fast_exact(gk)) h[e] = swiglu_f32(g[e], u[e]);
+            }
 #pragma unroll
         for (int e = 0; e < 16; e += 2) {
             const uint32_t b = pack_bf16(h[e], h[e + 1]);

@@ -268,7 +268,9 @@ def test_swiglu_rotate_quant_near_bf16_midpoints(cr):
     exponential of -g is near the top of the fp32 range.  Further rows, not
     picked near midpoints: g in [-120, -60] (for g <= -89 the definition's
     exponential overflows and its quotient is -0), and |g| near 2^60..2^70,
-    where the fast quotient overflows and the definition is taken."""
+    where the fast quotient overflows and the definition is taken.  Last,
+    exact ties g u for every bf16 gate in (16, 20): from 16.75 on the
+    quotient is g itself and the fast value is taken as it stands."""
     rng = np.random.default_rng(77)
     n = 1 << 24
     sig = rng.choice(np.array([0.3, 2.0, 6.0, 14.0, 40.0, 71.0], dtype=np.float32), n)
@@ -293,8 +295,16 @@ def test_swiglu_rotate_quant_near_bf16_midpoints(cr):
     huge_g = oracle.bf16_to_f32(workloads.to_bf16_bits(
         (rng.choice([-1.0, 1.0], 100) * np.exp2(rng.uniform(60.0, 70.0, 100))).astype(np.float32)))
     huge_u = oracle.bf16_to_f32(workloads.to_bf16_bits((1e-3 * rng.standard_normal(100)).astype(np.float32)))
-    g_pick = np.concatenate([g_pick, tail_g, huge_g])
-    u_pick = np.concatenate([u_pick, tail_u, huge_u])
+    # exact bf16 ties g u with g on the bf16 grid around 16.75, where
+    # 1 + exp(-g) first rounds to 1 and the quotient becomes g itself
+    edge_g = np.repeat(np.arange(16.125, 20.0, 0.125, dtype=np.float32), 4096)
+    edge_u = oracle.bf16_to_f32(workloads.to_bf16_bits(
+        rng.standard_normal(edge_g.size, dtype=np.float32) * rng.choice(np.array([1.0, 300.0], dtype=np.float32), edge_g.size)))
+    tie = ((edge_g.astype(np.float64) * edge_u).astype(np.float32).view(np.uint32) & 0xFFFF) == 0x8000
+    edge = np.nonzero(tie)[0]
+    assert edge.size > 500 and np.unique(edge_g[edge]).size == 31, edge.size
+    g_pick = np.concatenate([g_pick, tail_g, huge_g, edge_g[edge]])
+    u_pick = np.concatenate([u_pick, tail_u, huge_u, edge_u[edge]])
     m, i = g_pick.size, 256
     gu_rows = np.zeros((m, 2 * i), dtype=np.float32)
     cols = rng.integers(0, i, m)

@@ -31,6 +31,12 @@ HEADER = Path(__file__).resolve().parents[1] / "rotation_quantized_dit_amd" / "c
 f32 = np.float32
 
 
+def _exact_range():
+    """The gate range [lo, hi) that swiglu_fast_exact accepts, from the header."""
+    m = re.search(r"return g >= ([0-9.]+)f && g < (0x1p\d+)f;", HEADER.read_text())
+    return f32(float(m.group(1))), float.fromhex(m.group(2))
+
+
 def _header_constants():
     text = HEADER.read_text()
     c_hi = re.search(r"SWIGLU_C_HI\s*=\s*([-+0-9a-fA-Fx.p]+)f;", text).group(1)
@@ -141,3 +147,30 @@ def test_margin_decides_bf16_rounding():
     for delta in (-(margin // 2), -1, 1, margin // 2):
         moved = (bits.astype(np.int64) + delta).astype(np.uint32)
         assert np.array_equal(to_bf16(moved), base)
+
+
+@pytest.mark.parametrize("off_exp", [-2.0, 0.0, 2.0])
+def test_exact_quotient_range(off_exp):
+    """On every bf16 gate that swiglu_fast_exact accepts, the definition's
+    1 + exp(-g) rounds to 1 (so its quotient is g) and the fast d is exactly
+    2^-64 with exp2 pushed 2 ulps either way (so the fast quotient is
+    g 2^64 2^-64 = g); the bf16 gate just below the range has 1 + exp(-g) > 1."""
+    c_hi, c_lo, _ = _header_constants()
+    lo, hi = _exact_range()
+    g = _all_finite_bf16()
+    sel = (g >= lo) & (g < hi)
+    assert sel.sum() > 1000
+    with np.errstate(all="ignore"):
+        t = (g * c_hi).astype(np.float32)
+        a64 = np.exp2(t.astype(np.float64))
+        a = (a64 + np.where(np.isfinite(a64), off_exp * _ulp(np.minimum(a64, 3e38)), 0)).astype(np.float32)
+        e = (a.astype(np.float64) * (g * c_lo).astype(np.float64) + a.astype(np.float64)).astype(np.float32)
+        d = ((e.astype(np.float64) + 1.0) * 2.0 ** -64).astype(np.float32)
+    assert np.all(d[sel] == f32(2.0 ** -64))
+    # the largest accepted gate times 2^64 stays finite
+    assert np.isfinite(f32(g[sel].max()) * f32(2.0 ** 64))
+    one = np.array([f32(1) + f32(oracle.exp(-float(x))) for x in g[sel].tolist()], dtype=np.float32)
+    assert np.all(one == 1)
+    below = np.nextafter(lo, f32(0))                      # fp32 neighbour, then its bf16 floor
+    below = f32((np.array([below], dtype=np.float32).view(np.uint32) & 0xFFFF0000).view(np.float32)[0])
+    assert below < lo and f32(1) + f32(oracle.exp(-float(below))) > 1
