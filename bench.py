@@ -31,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "ConvRot int8 linear effective TOPS + % of int8 MFMA peak (hidden 5376 FFN)"
 PEAK_INT8_TOPS = 5000.0      # MI355X dense int8 MFMA, 5.0 POP/s
 PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+PEAK_FP4_TFLOPS = 10100.0    # MI355X dense FP4 MFMA, 10.1 PFLOP/s
 
 
 def log(msg):
@@ -115,7 +116,14 @@ def cpu_baseline(x_bits, w_up, w_dn, target_s=12.0, single_s=3.0):
             "host_cpus": os.cpu_count()}
 
 
-def attention_bench(torch, cr, dev, steps):
+def clock_scaled(frac, clock):
+    """frac of the rated peak -> frac of the peak at the sustained clock."""
+    if not clock:
+        return None
+    return round(frac * 2.4 / clock["clock_ghz"], 4)
+
+
+def attention_bench(torch, cr, dev, steps, with_clock=True):
     import workloads
     log("attention: generating inputs")
     att = workloads.make_attention()
@@ -162,6 +170,13 @@ def attention_bench(torch, cr, dev, steps):
                              "kernel's 1:1 mix; the kernel is bound by vector-instruction issue "
                              "(softmax, about 7 instructions per logit) rather than by MFMA"},
     }
+    # the clock the chip sustains under the flash kernel (live, amd-smi)
+    if with_clock:
+        log("attention: sampling the sustained clock")
+        clk = sustained_clock(torch, lambda: cr.attention_prepared(ws, S, H, out=o), flops, seconds=2.5)
+        res["sustained_clock"] = clk
+        res["roofline"]["clock_ghz"] = clk["clock_ghz"] if clk else None
+        res["roofline"]["frac_at_measured_clock"] = clock_scaled(res["roofline"]["frac"], clk)
     # context: torch's bf16 scaled-dot-product attention on the same tensors
     try:
         qh = q.reshape(S, H, D).transpose(0, 1).unsqueeze(0).contiguous()
@@ -309,7 +324,7 @@ def sustained_clock(torch, fn, ops, seconds=2.5):
                       "kernel ran back to back for %.1f s" % (t1 - t0)}
 
 
-def hybrid_bench(torch, cr, dev, steps):
+def hybrid_bench(torch, cr, dev, steps, with_clock=True):
     """One block's four projections at 32464 tokens (the block chain: 32256
     video + 208 audio tokens), int8 ConvRot everywhere against the MXFP4
     hybrid (QKV and FFN input in MXFP4, attention output and FFN output +
@@ -407,6 +422,22 @@ def hybrid_bench(torch, cr, dev, steps):
         res["change_pct"][name] = {k: round(100.0 * (am[k] / a8[k] - 1.0), 1) for k in a8}
         res["tflops_" + name] = {k: round(ops[k] / (am[k] * 1e-3) / 1e12, 1) for k in ops}
     res["int8_tops"] = {k: round(ops[k] / (a8[k] * 1e-3) / 1e12, 1) for k in ops}
+    # the MXFP4 GEMM alone on the FFN-input shape, back to back, with the
+    # clock the chip sustains under it (live, amd-smi)
+    if with_clock:
+        log("hybrid: sampling the sustained clock under the MXFP4 FFN-input GEMM")
+        x3 = workloads.chain_outliers(o2, idx[2])
+        a_codes, a_scales = cr.mx_quantize_act(x3)
+        w_codes, w_scales = mxw[False][1]
+        clk = sustained_clock(torch, lambda: cr.mx_gemm(a_codes, a_scales, w_codes, w_scales, out=gu_),
+                              ops["ffn_input"], seconds=2.5)
+        if clk:
+            frac = clk["TOPS"] / PEAK_FP4_TFLOPS
+            clk["frac"] = round(frac, 4)
+            clk["frac_at_measured_clock"] = clock_scaled(frac, clk)
+            clk["note"] = "TOPS here are FP4 TFLOP/s of the GEMM alone; frac against the 10.1 PFLOP/s dense FP4 peak"
+        res["mx_gemm_ffn_input_clock"] = clk
+        del a_codes, a_scales
     # the block chain with fc1's SwiGLU fused into its epilogue: per projection
     # (each including its rotate+quantize pass) and the four together
     fz = res["projections_ms"]["int8_convrot_fused_swiglu"]
@@ -751,8 +782,8 @@ def main():
     # 42 heads of 128 (the fused QKV layout, Q/K/V as column slices), timed as
     # prep (quantize Q, K; lay out V) and flash kernel; torch's bf16 SDPA on
     # the same shape for context.
-    attention = attention_bench(torch, cr, dev, args.steps)
-    hybrid = hybrid_bench(torch, cr, dev, args.steps)
+    attention = attention_bench(torch, cr, dev, args.steps, with_clock=not args.no_clock)
+    hybrid = hybrid_bench(torch, cr, dev, args.steps, with_clock=not args.no_clock)
     qkv = qkv_bench(torch, cr, dev, args.steps)
 
     # cross-check: the same step through the fused entry points (same kernels)
