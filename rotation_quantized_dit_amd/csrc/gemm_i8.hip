@@ -16,17 +16,26 @@
 //
 // Tiling.  A workgroup of 8 waves (two per SIMD) owns a 384 x 256 tile of acc
 // (384 tokens; for SwiGLU 128 gate columns + the matching 128 up columns).
-// Waves form a 4 (rows) x 2 (columns) grid; each owns 96 x 128 as 3 x 4 blocks
-// of v_mfma_i32_32x32x32_i8 (32 x 32 outputs, 32 bytes of K per instruction,
-// 16 int32 accumulators per lane per block, 192 in all).  For SwiGLU a wave's
+// Waves form a 4 (rows) x 2 (columns) grid; each owns 96 x 128 as 6 x 8 blocks
+// of v_mfma_i32_16x16x64_i8 (16 x 16 outputs, 64 bytes of K per instruction,
+// 4 int32 accumulators per lane per block, 192 in all).  For SwiGLU a wave's
 // 128 columns are 64 gate columns and the 64 up columns of the same outputs,
 // so every lane holds g and u of its elements.  Two waves per SIMD let the
 // matrix core take MFMAs from whichever wave has one ready while the other
 // waits on a fragment read, a copy or the stage barrier.
 //
+// Why 16 x 16 x 64.  The chip runs this kernel at its power limit, so the
+// rate is set by the energy per operation.  For the same int8 work and the
+// same LDS fragment bytes, the 16 x 16 form moves a quarter of the
+// accumulator bytes through the register file per operation (4 registers read
+// and written per 32 K ops against 16 per 64 K) and holds the higher clock:
+// a loop of either form at the power limit, with this kernel's fragment
+// traffic, sustained 3.35 against 2.96 POP/s, and this kernel runs 8-11 %
+// faster than the same design on v_mfma_i32_32x32x32_i8.
+
 // Operand streaming.  Both operands are K-contiguous rows (q_x is [M, K] and
 // q_w is [N, K]), which is the MFMA operand layout: a lane takes 16
-// contiguous bytes of one row.  K advances 64 bytes per stage through a ring
+// contiguous bytes of one row (row l % 16 of a 16-row block, chunk l / 16).  K advances 64 bytes per stage through a ring
 // of 4 LDS slots (40 KiB each, the whole 160 KiB).  Global -> LDS copies are
 // direct buffer loads (buffer_load_dwordx4 ... lds: 64 lanes x 16 B land
 // contiguously in LDS, no VGPR staging): each wave copies 48 rows of A and 32
@@ -44,20 +53,22 @@
 // the LDS destination, is passed as an input operand, so the compiler knows
 // it is set.
 //
-// Main loop (one stage = two k-steps of 12 MFMAs per wave), unrolled over
-// the four slots of the ring so that every LDS offset is an immediate (K is
-// a multiple of 256, so the stage count is a multiple of four):
-//   - the MFMAs run in a fixed order (A0 x B0..B3, then A1/A2 alternating
-//     over B0..B3), and each fragment register is refilled with the next
-//     k-step's fragment right after its last use, which spreads the seven
-//     reads over the k-step and gives each at least four MFMAs of latency;
-//   - the stage barrier sits after the fourth MFMA of the second k-step, so
-//     each wave enters it with MFMAs in flight; before it, a vmcnt wait
-//     makes this wave's copies of the next stage complete, and lgkmcnt(0)
-//     makes its reads of the current slot complete;
+// Main loop (one stage = 48 MFMAs per wave, 64 bytes of K), unrolled over the
+// four slots of the ring (K is a multiple of 256, so the stage count is a
+// multiple of four):
+//   - the stage runs as 8 phases, one per B block j: every A block times B
+//     block j.  The six A fragments stay in registers for the stage and B is
+//     double-buffered, B block j + 1 read at the start of phase j (224
+//     registers of accumulators and fragments);
+//   - the stage barrier sits after the fourth MFMA of phase 6, so each wave
+//     enters it with MFMAs in flight; before it, a vmcnt wait makes this
+//     wave's copies of the next stage complete, and lgkmcnt(0) makes its
+//     reads of the current slot complete;
+//   - phase 7 then reads the next slot: its first B block at the phase's
+//     start and each A block right after that block's last MFMA;
 //   - after the barrier the current slot is refilled with the stage four
-//     ahead: three copies spread over the rest of that k-step, the last two
-//     in the next stage's first k-step.
+//     ahead: three copies spread over the rest of the stage, the last two
+//     in the next stage's first phases.
 // Past the last stage the copies are still issued (so every stage has the
 // same shape and the vmcnt counts stay uniform) but with the voffset
 // pushed beyond the buffer's range: the hardware returns zeros without a
@@ -85,7 +96,10 @@ namespace {
 constexpr int BM = 384;               // tile rows (tokens): 4 wave rows x 96
 constexpr int BN = 256;               // tile columns (weight rows)
 constexpr int BK = 64;                // K bytes per stage
-constexpr int MA = 3;                 // 32-row A blocks per wave
+constexpr int WROWS = 96;             // tile rows per wave (BM / 4)
+constexpr int A_COPIES = 3;           // 16-row copies of A per wave per stage (WROWS / 2 / 16)
+constexpr int NA = 6;                 // 16-row A blocks per wave (MFMA rows)
+constexpr int NB = 8;                 // 16-column B blocks per wave (MFMA columns)
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int A_STAGE = BM * BK;
@@ -93,8 +107,8 @@ constexpr int B_STAGE = BN * BK;
 constexpr int STAGE_BYTES = A_STAGE + B_STAGE;
 constexpr int STAGES = 4;
 constexpr int RING_BYTES = STAGES * STAGE_BYTES;
-// copies per wave per stage: MA of A (16 rows each) and 2 of B
-constexpr int COPIES = MA + 2;
+// copies per wave per stage: A_COPIES of A (16 rows each) and 2 of B
+constexpr int COPIES = A_COPIES + 2;
 // copies of a refill issued in the k-step after the stage barrier; the rest
 // go out in the next stage's first k-step
 constexpr int COPIES_NOW = 3;
@@ -102,8 +116,8 @@ constexpr int COPIES_NOW = 3;
 // ring's memory (bf16 outputs as bf16; the int32 output as int32, rows
 // padded to PITCH int32 to spread banks), and the tile's row scales follow
 // the largest of those areas.
-constexpr int PITCH = 136;
-constexpr int STASH_WAVE_BYTES = 32 * PITCH * 4;
+constexpr int PITCH = 140;
+constexpr int STASH_WAVE_BYTES = 16 * PITCH * 4;
 constexpr int STASH_BYTES = NWAVES * STASH_WAVE_BYTES;
 constexpr int SX_OFFSET = STASH_BYTES;
 constexpr int GROUP_M = 2;            // M-tiles per raster group
@@ -116,7 +130,14 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+// a + b for a lane value a and a constant b, computed where it stands (the
+// compiler neither hoists nor folds it)
+template <int B>
+__device__ __forceinline__ int opaque_add(int a) {
+    int r;
+    asm volatile("v_add_u32_e32 %0, %2, %1" : "=v"(r) : "v"(a), "i"(B));
+    return r;
+}
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
 // vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[15:14]).
@@ -232,8 +253,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         if (tid < BM) sx_own = sx[tid < rows_a ? m0 + tid : M - 1];
     }
 
-    // Copy sources.  Copy i < MA of wave w fills A slab rows 16 (MA w + i) ..
-    // +15 of a stage; copy MA + i (i = 0, 1) fills B slab rows 32 w + 16 i ..
+    // Copy sources.  Copy i < A_COPIES of wave w fills A slab rows
+    // 16 (A_COPIES w + i) .. +15 of a stage; copy A_COPIES + i (i = 0, 1)
+    // fills B slab rows 32 w + 16 i ..
     // +15.  Lane l writes row (l / 4) of its 16 at chunk position l % 4,
     // which holds logical chunk (l % 4) ^ swz(row).  Offsets are relative to a
     // per-panel buffer resource (the tile's A rows; its gate rows; its up
@@ -259,53 +281,43 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     // outputs are masked at the store).  A wave's copies are 16 rows apart
     // and share one swizzle, ((r >> 2) & 3) = ((lane >> 4) & 3).
     const uint32_t chunk = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
-    const uint32_t voff_a = (uint32_t)(16 * MA * wave + (lane >> 2)) * (uint32_t)K + chunk;
+    const uint32_t voff_a = (uint32_t)(16 * A_COPIES * wave + (lane >> 2)) * (uint32_t)K + chunk;
     const uint32_t voff_b = (uint32_t)(32 * (EP == Epilogue::SWIGLU ? (wave & 3) : wave) + (lane >> 2)) * (uint32_t)K + chunk;
     const uint32_t row16 = 16u * (uint32_t)K;
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(__attribute__((address_space(3))) int8_t*)lds);
     // copy i of the stage at K byte soff into ring slot `slot` (oob: 0 or OOB)
     auto issue = [&](int i, uint32_t soff, uint32_t oob, int slot) {
-        const uint32_t dst = i < MA ? lds_base + slot * STAGE_BYTES + 1024 * (MA * wave + i)
-                                    : lds_base + slot * STAGE_BYTES + A_STAGE + 2048 * wave + 1024 * (i - MA);
-        const uint32_t vo = i < MA ? voff_a + (uint32_t)i * row16 : voff_b + (uint32_t)(i - MA) * row16;
-        copy16(i < MA ? rsrc_a : rsrc_b, dst, vo + oob, soff);
+        const uint32_t dst = i < A_COPIES
+                                 ? lds_base + slot * STAGE_BYTES + 1024 * (A_COPIES * wave + i)
+                                 : lds_base + slot * STAGE_BYTES + A_STAGE + 2048 * wave + 1024 * (i - A_COPIES);
+        const uint32_t vo = i < A_COPIES ? voff_a + (uint32_t)i * row16 : voff_b + (uint32_t)(i - A_COPIES) * row16;
+        copy16(i < A_COPIES ? rsrc_a : rsrc_b, dst, vo + oob, soff);
     };
 
-    // LDS rows of this lane's fragments: A blocks a < MA (rows of the wave's
-    // band), B blocks b = 0..3 (for SwiGLU: b = 0, 1 gate, 2, 3 up).
-    int a_row[MA], b_row[4];
-#pragma unroll
-    for (int a = 0; a < MA; ++a) a_row[a] = 32 * MA * wm + 32 * a + (lane & 31);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        if constexpr (EP == Epilogue::SWIGLU)
-            b_row[b] = (b < 2 ? 0 : 128) + 64 * wn + 32 * (b & 1) + (lane & 31);
-        else
-            b_row[b] = 128 * wn + 32 * b + (lane & 31);
-    }
-    // Byte offsets (within a stage) of this lane's 16-byte fragment reads for
-    // the two 32-byte k-steps of a stage.
-    int a_off[2][MA], b_off[2][4];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-        const int c = 2 * s + (lane >> 5);
-#pragma unroll
-        for (int a = 0; a < MA; ++a) a_off[s][a] = a_row[a] * BK + 16 * (c ^ swz(a_row[a]));
-#pragma unroll
-        for (int b = 0; b < 4; ++b) b_off[s][b] = A_STAGE + b_row[b] * BK + 16 * (c ^ swz(b_row[b]));
-    }
+    // Fragment reads.  v_mfma_i32_16x16x64_i8 takes, in lane l, row l % 16 of
+    // a 16-row block and the 16 bytes of K at chunk l / 16 of the stage's 64.
+    // Every block starts at a row that is a multiple of 16, so the swizzle
+    // (row >> 2) & 3 depends on the lane alone and block i of a panel lies
+    // 1 KiB after block i - 1: one base offset per operand.
+    const int fr = lane & 15;
+    const int fpos = 16 * ((lane >> 4) ^ ((fr >> 2) & 3));
+    const int a_base = (WROWS * wm + fr) * BK + fpos;
+    const int b_base = A_STAGE + ((EP == Epilogue::SWIGLU ? 64 : 128) * wn + fr) * BK + fpos;
+    // B block j of the wave: rows 16 j of its 128 (BF16, S32); for SwiGLU
+    // blocks 0-3 are gate rows 64 wn + 16 j and blocks 4-7 the up rows of the
+    // same outputs, 128 rows further
+    constexpr int BOFF[NB] = {0, 1, 2, 3, EP == Epilogue::SWIGLU ? 8 : 4, EP == Epilogue::SWIGLU ? 9 : 5,
+                              EP == Epilogue::SWIGLU ? 10 : 6, EP == Epilogue::SWIGLU ? 11 : 7};
 
-    v16i acc[MA][4];
+    v4i acc[NA][NB];
 #pragma unroll
-    for (int a = 0; a < MA; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0;
+        for (int b = 0; b < NB; ++b) acc[a][b] = v4i{0, 0, 0, 0};
 
     // Prologue: fill every slot (stages past the last go out of range), wait
-    // for stage 0, read its first k-step's fragments.
+    // for stage 0, read its A fragments and its first B fragment.
     const int KT = K / BK;
 #pragma unroll
     for (int st = 0; st < STAGES; ++st)
@@ -313,44 +325,30 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         for (int i = 0; i < COPIES; ++i) issue(i, (uint32_t)st * BK, st < KT ? 0u : OOB, st);
     wait_vmcnt<(STAGES - 1) * COPIES>();
     lds_barrier();
-    v4i fa[MA], fb[4];
+    v4i fa[NA], fb[2];
 #pragma unroll
-    for (int a = 0; a < MA; ++a) fa[a] = *reinterpret_cast<const v4i*>(lds + a_off[0][a]);
-#pragma unroll
-    for (int b = 0; b < 4; ++b) fb[b] = *reinterpret_cast<const v4i*>(lds + b_off[0][b]);
+    for (int a = 0; a < NA; ++a) fa[a] = *reinterpret_cast<const v4i*>(lds + a_base + 1024 * a);
+    fb[0] = *reinterpret_cast<const v4i*>(lds + b_base);
     // nothing of the prologue (scalar loads included) stays pending in
     // lgkmcnt, so the loop's waits on its fragment reads can be exact
     wait_lds_reads();
     __builtin_amdgcn_sched_barrier(0);
 
-    // The fixed MFMA order of a k-step (slot i: A block SA[i] x B block SB[i])
-    // and the refill points: A0 after slot 3, B0 after 5, B1 after 7, B2
-    // after 9, B3, A1 and A2 after 11.
-    constexpr int SA[12] = {0, 0, 0, 0, 1, 2, 1, 2, 1, 2, 1, 2};
-    constexpr int SB[12] = {0, 1, 2, 3, 0, 0, 1, 1, 2, 2, 3, 3};
-    auto mfma = [&](int i) {
-        acc[SA[i]][SB[i]] = __builtin_amdgcn_mfma_i32_32x32x32_i8(fa[SA[i]], fb[SB[i]], acc[SA[i]][SB[i]], 0, 0, 0);
-    };
-    auto refill = [&](int i, const int8_t* st, int s) {
-        if (i == 3) fa[0] = *reinterpret_cast<const v4i*>(st + a_off[s][0]);
-        if (i == 5) fb[0] = *reinterpret_cast<const v4i*>(st + b_off[s][0]);
-        if (i == 7) fb[1] = *reinterpret_cast<const v4i*>(st + b_off[s][1]);
-        if (i == 9) fb[2] = *reinterpret_cast<const v4i*>(st + b_off[s][2]);
-        if (i == 11) {
-            fb[3] = *reinterpret_cast<const v4i*>(st + b_off[s][3]);
-            fa[1] = *reinterpret_cast<const v4i*>(st + a_off[s][1]);
-            fa[2] = *reinterpret_cast<const v4i*>(st + a_off[s][2]);
-        }
-    };
-    // copy j (< COPIES_NOW) of a refill goes out after slot CS[j] of the
-    // k-step that follows the barrier; copies COPIES_NOW.. after slots 0 and 6
-    // of the next stage's first k-step
-    constexpr int CS[COPIES_NOW] = {4, 7, 10};
-    constexpr int BARRIER_AFTER = 3;
+    // A stage is NB phases of NA MFMAs: phase j multiplies every A block with
+    // B block j (in fb[j & 1]), and B block j + 1 is read at the start of
+    // phase j.  The stage barrier follows MFMA BARRIER_AT (in phase NB - 2);
+    // phase NB - 1 then reads the next slot: its first B block at the phase's
+    // start and each A block right after that block's last MFMA.
+    constexpr int BARRIER_AT = NA * (NB - 2) + 3;
+    // copy j (< COPIES_NOW) of a refill goes out after MFMA CS[j] of the
+    // stage, after the barrier; copies COPIES_NOW.. after MFMAs 0 and 12 of
+    // the next stage
+    constexpr int CS[COPIES_NOW] = {BARRIER_AT + 2, BARRIER_AT + 4, BARRIER_AT + 6};
+    static_assert(BARRIER_AT + 6 < NA * NB, "copies inside the stage");
 
-    // One stage with its ring slot known at compile time (every LDS offset an
-    // immediate); K is a multiple of 256, so the stage count is a multiple
-    // of STAGES and the loop runs whole rounds.
+    // One stage with its ring slot known at compile time; K is a multiple of
+    // 256, so the stage count is a multiple of STAGES and the loop runs whole
+    // rounds.
     static_assert(256 % (STAGES * BK) == 0, "whole rounds of STAGES stages");
     auto stage = [&](auto slot_c, int kt) {
         constexpr int slot = decltype(slot_c)::value;
@@ -362,37 +360,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         const uint32_t prev_soff = kt > 0 ? (uint32_t)(kt - 1 + STAGES) * BK : (uint32_t)(STAGES - 1) * BK;
         const uint32_t prev_oob = kt > 0 && kt - 1 + STAGES >= KT ? OOB : 0u;
         const uint32_t soff = (uint32_t)(kt + STAGES) * BK;
-        const int8_t* cur = lds + slot * STAGE_BYTES;
-        const int8_t* nxt = lds + next * STAGE_BYTES;
+        // fragment bases in this stage's slot (B only) and the next stage's,
+        // formed here by an opaque add so that the compiler keeps three
+        // registers rather than one per slot and block across the loop
+        const int8_t* cur_b = lds + opaque_add<slot * STAGE_BYTES>(b_base);
+        const int8_t* nxt_a = lds + opaque_add<next * STAGE_BYTES>(a_base);
+        const int8_t* nxt_b = lds + opaque_add<next * STAGE_BYTES>(b_base);
 #pragma unroll
-        for (int i = 0; i < 12; ++i) {
-            __builtin_amdgcn_sched_barrier(0);
-            mfma(i);
-            refill(i, cur, 1);
-            if (i == 0) issue(COPIES_NOW, prev_soff, prev_oob, prev_slot);
-            if (i == 6) issue(COPIES_NOW + 1, prev_soff, prev_oob, prev_slot);
-        }
+        for (int j = 0; j < NB; ++j) {
 #pragma unroll
-        for (int i = 0; i <= BARRIER_AFTER; ++i) {
-            __builtin_amdgcn_sched_barrier(0);
-            mfma(i);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<(STAGES - 2) * COPIES>();
-        lds_barrier();
+            for (int i = 0; i < NA; ++i) {
+                const int idx = NA * j + i;
+                __builtin_amdgcn_sched_barrier(0);
+                acc[i][j] = __builtin_amdgcn_mfma_i32_16x16x64_i8(fa[i], fb[j & 1], acc[i][j], 0, 0, 0);
+                if (i == 0 && j + 1 < NB)
+                    fb[(j + 1) & 1] = *reinterpret_cast<const v4i*>(cur_b + 1024 * BOFF[j + 1]);
+                if (idx == 0) issue(COPIES_NOW, prev_soff, prev_oob, prev_slot);
+                if (idx == 12) issue(COPIES_NOW + 1, prev_soff, prev_oob, prev_slot);
+                if (idx == BARRIER_AT) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    wait_vmcnt<(STAGES - 2) * COPIES>();
+                    lds_barrier();
+                }
+                if (j == NB - 1) {
+                    if (i == 0) fb[0] = *reinterpret_cast<const v4i*>(nxt_b);
+                    fa[i] = *reinterpret_cast<const v4i*>(nxt_a + 1024 * i);
+                }
 #pragma unroll
-        for (int i = 0; i < 12; ++i) {
-            __builtin_amdgcn_sched_barrier(0);
-            if (i > BARRIER_AFTER) mfma(i);
-            if (i == BARRIER_AFTER) {
-#pragma unroll
-                for (int j = 0; j <= BARRIER_AFTER; ++j) refill(j, nxt, 0);
-            } else if (i > BARRIER_AFTER) {
-                refill(i, nxt, 0);
+                for (int c = 0; c < COPIES_NOW; ++c)
+                    if (CS[c] == idx) issue(c, soff, oob, slot);
             }
-#pragma unroll
-            for (int j = 0; j < COPIES_NOW; ++j)
-                if (CS[j] == i) issue(j, soff, oob, slot);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -411,29 +408,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     for (int i = COPIES_NOW; i < COPIES; ++i) issue(i, prev_soff, OOB, prev_slot);
     wait_vmcnt<0>();
 
-    // Epilogue.  Block (a, b), lane l, register r of the MFMA accumulators
-    // holds row 32 a + 8 (r / 4) + 4 (l / 32) + r % 4 and column 32 b + l % 32
-    // of the wave's 96 x 128 sub-tile.  For bf16 outputs each lane forms its
-    // values where they lie (dequant, and for SwiGLU silu(g) u from the gate
-    // block b and the up block b + 2 of the same outputs) and parks them as
-    // bf16 in its wave's part of the (now free) ring, 32 rows at a time;
-    // the rows are then read back contiguous, 16 bytes per lane, and leave
-    // as one 16-byte store.  The int32 output parks the accumulators
+    // Epilogue.  Block (a, b), lane l, register r of the accumulators holds
+    // row 16 a + 4 (l / 16) + r and column 16 b + l % 16 of the wave's
+    // 96 x 128 sub-tile; for SwiGLU block b < 4 holds the gate and block
+    // b + 4 the up value of output column 16 b + l % 16 of the wave's 64.
+    // For bf16 outputs each lane forms its values where they lie and parks
+    // them as bf16 in its wave's part of the (now free) ring, 16 rows at a
+    // time; the rows are then read back contiguous, 16 bytes per lane, and
+    // leave as one 16-byte store.  The int32 output parks the accumulators
     // themselves.
-    const int l31 = lane & 31, hl = lane >> 5;
-    // s_w of the lane's accumulator columns: b = 0..3 (BF16), or the gate
-    // (b = 0, 1) and up (b = 2, 3) rows of h column 32 (b & 1) + l % 32
-    float swv[4];
+    const int q4 = lane >> 4;
+    float swv[NB];
     if constexpr (EP != Epilogue::S32) {
 #pragma unroll
-        for (int bb = 0; bb < 4; ++bb) {
+        for (int b = 0; b < NB; ++b) {
             int c;
             if constexpr (EP == Epilogue::SWIGLU)
-                c = tile.tn * (BN / 2) + 64 * wn + 32 * (bb & 1) + l31;
+                c = tile.tn * (BN / 2) + 64 * wn + 16 * (b & 3) + fr;
             else
-                c = tile.tn * BN + 128 * wn + 32 * bb + l31;
+                c = tile.tn * BN + 128 * wn + 16 * b + fr;
             c = c < N ? c : N - 1;
-            swv[bb] = sw[(EP == Epilogue::SWIGLU && bb >= 2 ? N : 0) + c];
+            swv[b] = sw[(EP == Epilogue::SWIGLU && b >= 4 ? N : 0) + c];
         }
     }
     lds_barrier();   // every wave is done reading the ring
@@ -442,7 +437,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         if (tid < BM) sx_lds[tid] = sx_own;
         lds_barrier();
     }
-    const int grow0 = m0 + 32 * MA * wm;
+    const int grow0 = m0 + WROWS * wm;
     const int col0 = epi_col0;
     const int cg = epi_cg;
     const int ro = epi_ro;
@@ -452,18 +447,17 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         int32_t* stash = reinterpret_cast<int32_t*>(lds + wave * STASH_WAVE_BYTES);
         int32_t* o = reinterpret_cast<int32_t*>(out);
 #pragma unroll
-        for (int a = 0; a < MA; ++a) {
+        for (int a = 0; a < NA; ++a) {
             asm volatile("" ::: "memory");
 #pragma unroll
-            for (int bb = 0; bb < 4; ++bb)
+            for (int b = 0; b < NB; ++b)
 #pragma unroll
-                for (int r = 0; r < 16; ++r)
-                    stash[(8 * (r >> 2) + 4 * hl + (r & 3)) * PITCH + 32 * bb + l31] = acc[a][bb][r];
+                for (int r = 0; r < 4; ++r) stash[(4 * q4 + r) * PITCH + 16 * b + fr] = acc[a][b][r];
             asm volatile("" ::: "memory");
 #pragma nounroll
-            for (int it = 0; it < 8; ++it) {
+            for (int it = 0; it < 4; ++it) {
                 const int lr = 4 * it + ro;
-                const int grow = grow0 + 32 * a + lr;
+                const int grow = grow0 + 16 * a + lr;
                 const v4i a0 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg);
                 const v4i a1 = *reinterpret_cast<const v4i*>(stash + lr * PITCH + 8 * cg + 4);
                 if (grow >= M) continue;
@@ -480,50 +474,43 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         }
     } else {
         // bf16 rows of 64 (SwiGLU) or 128 outputs, padded to P16 bf16 so that
-        // the two lane halves (rows r and r + 4) write disjoint banks
-        constexpr int NB = EP == Epilogue::SWIGLU ? 2 : 4;     // output blocks per wave row
-        constexpr int P16 = 32 * NB + 8;
-        constexpr int ITS = EP == Epilogue::SWIGLU ? 4 : 8;    // read-back rows per lane
-        constexpr int ROW_STEP = 32 / ITS;
-        uint16_t* st16 = reinterpret_cast<uint16_t*>(lds + wave * (32 * P16 * 2));
+        // the four lane quarters (rows 4 apart) write disjoint banks
+        constexpr int NBO = EP == Epilogue::SWIGLU ? 4 : 8;    // output blocks per wave row
+        constexpr int P16 = 16 * NBO + 8;
+        constexpr int ROW_STEP = EP == Epilogue::SWIGLU ? 8 : 4;   // rows per read-back
+        constexpr int ITS = 16 / ROW_STEP;
+        uint16_t* st16 = reinterpret_cast<uint16_t*>(lds + wave * (16 * P16 * 2));
         uint16_t* y = reinterpret_cast<uint16_t*>(out);
 #pragma unroll
-        for (int a = 0; a < MA; ++a) {
-            // row scales of the lane's 16 rows: 32 a + 8 q + 4 (l / 32) + p
-            float sxr[16];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const v4f t4 = *reinterpret_cast<const v4f*>(sx_lds + 32 * MA * wm + 32 * a + 8 * q + 4 * hl);
-                sxr[4 * q] = t4.x;
-                sxr[4 * q + 1] = t4.y;
-                sxr[4 * q + 2] = t4.z;
-                sxr[4 * q + 3] = t4.w;
-            }
+        for (int a = 0; a < NA; ++a) {
+            // row scales of the lane's rows 16 a + 4 (l / 16) + r
+            const v4f s4 = *reinterpret_cast<const v4f*>(sx_lds + WROWS * wm + 16 * a + 4 * q4);
+            const float sxr[4] = {s4.x, s4.y, s4.z, s4.w};
             asm volatile("" ::: "memory");
 #pragma unroll
-            for (int bb = 0; bb < NB; ++bb)
+            for (int bb = 0; bb < NBO; ++bb)
 #pragma unroll
-                for (int r = 0; r < 16; r += 2) {
+                for (int r = 0; r < 4; r += 2) {
                     float v0, v1;
                     if constexpr (EP == Epilogue::SWIGLU) {
                         v0 = swiglu_hw(dequant(acc[a][bb][r], sxr[r], swv[bb]),
-                                       dequant(acc[a][bb + 2][r], sxr[r], swv[bb + 2]));
+                                       dequant(acc[a][bb + 4][r], sxr[r], swv[bb + 4]));
                         v1 = swiglu_hw(dequant(acc[a][bb][r + 1], sxr[r + 1], swv[bb]),
-                                       dequant(acc[a][bb + 2][r + 1], sxr[r + 1], swv[bb + 2]));
+                                       dequant(acc[a][bb + 4][r + 1], sxr[r + 1], swv[bb + 4]));
                     } else {
                         v0 = dequant(acc[a][bb][r], sxr[r], swv[bb]);
                         v1 = dequant(acc[a][bb][r + 1], sxr[r + 1], swv[bb]);
                     }
                     const uint32_t pk = pack_bf16(v0, v1);
-                    const int row = 8 * (r >> 2) + 4 * hl + (r & 3);   // rows row, row + 1
-                    st16[row * P16 + 32 * bb + l31] = (uint16_t)pk;
-                    st16[(row + 1) * P16 + 32 * bb + l31] = (uint16_t)(pk >> 16);
+                    const int row = 4 * q4 + r;   // rows row, row + 1
+                    st16[row * P16 + 16 * bb + fr] = (uint16_t)pk;
+                    st16[(row + 1) * P16 + 16 * bb + fr] = (uint16_t)(pk >> 16);
                 }
             asm volatile("" ::: "memory");
 #pragma unroll
             for (int it = 0; it < ITS; ++it) {
                 const int lr = ROW_STEP * it + ro;
-                const int grow = grow0 + 32 * a + lr;
+                const int grow = grow0 + 16 * a + lr;
                 const v4u pk = *reinterpret_cast<const v4u*>(st16 + lr * P16 + 8 * cg);
                 if (grow < M) {
                     if (vec_cols) {
