@@ -1,5 +1,5 @@
 // MXFP4 x MXFP4 -> fp32 GEMM with a bf16 epilogue on the gfx950 scaled
-// MFMA (v_mfma_scale_f32_32x32x64_f8f6f4, both operands FP4 E2M1), for the
+// MFMA (v_mfma_scale_f32_16x16x128_f8f6f4, both operands FP4 E2M1), for the
 // MXFP4 analog of the hybrid layers (Minimax_h3_hybrid model card,
 // "Checkpoints": QKV and the FFN input in a 4-bit block format).
 //
@@ -10,27 +10,27 @@
 // Operands: codes [rows, K/2] bytes (element 2j in the low nibble of byte j)
 // and E8M0 scales chunk-major, [K/128][rows][4] bytes (the 4 block scales of
 // one 128-element chunk of consecutive rows are contiguous).  In bytes, a
-// 64-element k-step of FP4 occupies 32 bytes of a row and each lane takes 16
-// of them (lanes 0-31 the first 32 elements, lanes 32-63 the next 32),
-// exactly the layout of the int8 operands of K-GEMM, so the tiling is that
-// kernel's: a 384 x 256 tile, 8 waves (two per SIMD) in a 4 x 2 grid of
-// 96 x 128 wave tiles (3 x 4 MFMA blocks, 192 fp32 accumulators per lane),
-// 64 bytes (128 elements) of K per stage through a 3-slot LDS ring of direct
-// buffer loads, XOR-swizzled 64-byte rows, one fragment set per k-step.
-// The 96 x 128 wave tile reads 7 fragments per 12 MFMAs (against 6 per 8
-// for 64 x 128) and the 384-row tile copies 17 % fewer bytes per flop than a
-// 256-row one; both measured about 8 % faster on the FFN-input shape.
+// 128-element k-step of FP4 occupies 64 bytes of a row and each lane of a
+// 16-row block takes 16 of them (lane l: row l % 16, 32-element block l / 16),
+// exactly the layout of the int8 operands of K-GEMM (64 bytes of K per
+// v_mfma_i32_16x16x64_i8), so the tiling is that kernel's: a 384 x 256 tile,
+// 8 waves (two per SIMD) in a 4 x 2 grid of 96 x 128 wave tiles (6 x 8 MFMA
+// blocks, 192 fp32 accumulators per lane), one MFMA k-step (64 bytes, 128
+// elements) per stage through a 3-slot LDS ring of direct buffer loads,
+// XOR-swizzled 64-byte rows.  The 384-row tile copies 17 % fewer bytes per
+// flop than a 256-row one and measured about 8 % faster on the FFN-input
+// shape (with the 32 x 32 x 64 form of the MFMA).
 //
 // The main loop has the int8 kernel's schedule: copies issued from inline
-// assembly (so the compiler does not drain them before every fragment read),
-// a fixed MFMA order with each fragment register (and its block scale)
-// refilled right after its last use, the stage barrier after the fourth MFMA
-// of the second k-step, four of the six refill copies spread over that
-// k-step and the other two in the next stage's first k-step, copies
-// past the last stage pushed out of the buffer's range, and the stage loop
-// unrolled over the ring's three slots so that every LDS offset is an
-// immediate (without that the slot arithmetic needs registers the loop does
-// not have).
+// assembly (so the compiler does not drain them before every fragment read);
+// each stage as 8 phases, one per B block, with the six A fragments held for
+// the stage and B double-buffered; the stage barrier after the fourth MFMA of
+// the seventh phase; the last phase reading the next slot; four of the six
+// refill copies after the barrier and the other two in the next stage's first
+// phases; copies past the last stage pushed out of the buffer's range; the
+// stage loop unrolled over the ring's three slots.  Against the 32 x 32 x 64
+// form of the same design it measured 0-2 % faster, and its main loop holds
+// every value in registers.
 //
 // Each stage also carries the tile's scale words (one 32-bit word per row:
 // the 4 block scales of its 128 elements), 384 + 256 words copied as three
@@ -38,8 +38,8 @@
 // 1's copy reads rows past the tile into unused space), wave 2 the B rows.
 // So that the copy needs no branch, waves 3-7 issue the same load on an
 // empty buffer resource (every lane out of range: no memory is read) into a
-// spare 1 KiB of LDS.  For k-step s a lane reads the one byte it needs,
-// block 2 s + lane / 32 of its row, with a byte load from LDS.
+// spare 1 KiB of LDS.  For each fragment a lane reads the one scale byte it
+// needs, block l / 16 of its row, with a byte load from LDS.
 //
 // Ragged rows lie past their panel's buffer range, load as zeros and are
 // masked at the store; K must be a multiple of 128.
@@ -57,7 +57,9 @@ namespace {
 constexpr int BM = 384;
 constexpr int BN = 256;
 constexpr int BK = 64;                       // bytes of codes per row per stage (128 elements)
-constexpr int MA = BM / 128;                 // 32-row A blocks per wave
+constexpr int MA = BM / 128;                 // 16-row copies of A per wave per stage (96 rows / 32)
+constexpr int NA = 6;                        // 16-row A blocks per wave (MFMA rows)
+constexpr int NB = 8;                        // 16-column B blocks per wave (MFMA columns)
 constexpr int NWAVES = 8;
 constexpr int NTHREADS = 64 * NWAVES;
 constexpr int A_STAGE = BM * BK;
@@ -68,9 +70,9 @@ constexpr int STAGE_BYTES = A_STAGE + B_STAGE + SA_BYTES + SB_BYTES;
 constexpr int STAGES = 3;
 constexpr int COPIES = MA + 3;               // per wave per stage: A, B and one scale copy
 constexpr int SPARE = STAGES * STAGE_BYTES;  // 1 KiB that the idle scale copies fill
-// epilogue: each wave parks 32 rows x 128 bf16 at a time, rows padded to P16
+// epilogue: each wave parks 16 rows x 128 bf16 at a time, rows padded to P16
 constexpr int P16 = 136;
-constexpr int STASH_BYTES = NWAVES * 32 * P16 * 2;
+constexpr int STASH_BYTES = NWAVES * 16 * P16 * 2;
 constexpr int RING_BYTES = STAGES * STAGE_BYTES;
 constexpr int LDS_BYTES = RING_BYTES + 1024 > STASH_BYTES ? RING_BYTES + 1024 : STASH_BYTES;   // ring + spare
 constexpr int GROUP_M = 4;                   // M-tiles per raster group
@@ -80,10 +82,7 @@ static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
-typedef float v16f __attribute__((ext_vector_type(16)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
 
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -144,7 +143,6 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
     const int tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int lane = tid & 63;
-    const int g = lane >> 5;
     const int wm = wave >> 1;
     const int wn = wave & 1;
     const Tile tile = map_tile(blockIdx.x, MT, NT);
@@ -187,26 +185,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
         else dma16(rsrc_s, (wave < 3 ? st : lds_base) + s_dst, voff_s + oob, (uint32_t)kt * chunk_stride);
     };
 
-    v16f acc[MA][4];
+    v4f acc[NA][NB];
 #pragma unroll
-    for (int a = 0; a < MA; ++a)
+    for (int a = 0; a < NA; ++a)
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.0f;
+        for (int b = 0; b < NB; ++b) acc[a][b] = v4f{0.0f, 0.0f, 0.0f, 0.0f};
 
-    // Per-lane byte offsets within a stage.  The swizzle of every fragment
-    // row of a lane is (lane >> 2) & 3 (the rows differ by multiples of 32),
-    // so each operand needs one lane offset per k-step, the blocks following
-    // at fixed distances (2048 bytes per 32 code rows, 128 per 32 scale words).
-    const int sw = swz(lane & 31);
-    const int a_lane = (32 * MA * wm + (lane & 31)) * BK;
-    const int b_lane = A_STAGE + (128 * wn + (lane & 31)) * BK;
-    // A row's scale word holds the block scales of its 128 elements; the
-    // lanes of half g use block 2 s + g in k-step s (one byte read).
-    const int sa_byte = A_STAGE + B_STAGE + 4 * (32 * MA * wm + (lane & 31)) + g;
-    const int sb_byte = A_STAGE + B_STAGE + SA_BYTES + 4 * (128 * wn + (lane & 31)) + g;
-    const int c0 = 16 * ((0 + g) ^ sw), c1 = 16 * ((2 + g) ^ sw);
+    // Fragment reads.  v_mfma_scale_f32_16x16x128_f8f6f4 with FP4 operands
+    // takes, in lane l, row l % 16 of a 16-row block and the 32 elements (16
+    // bytes) of block l / 16 of the stage's 128, with that block's scale.
+    // Every block starts at a row that is a multiple of 16, so the swizzle
+    // (row >> 2) & 3 depends on the lane alone and block i of a panel lies
+    // 1 KiB (codes) or 64 bytes (scale words) after block i - 1.
+    const int fr = lane & 15;
+    const int fpos = 16 * ((lane >> 4) ^ ((fr >> 2) & 3));
+    const int a_base = (32 * MA * wm + fr) * BK + fpos;
+    const int b_base = A_STAGE + (128 * wn + fr) * BK + fpos;
+    const int sa_base = A_STAGE + B_STAGE + 4 * (32 * MA * wm + fr) + (lane >> 4);
+    const int sb_base = A_STAGE + B_STAGE + SA_BYTES + 4 * (128 * wn + fr) + (lane >> 4);
 
 #pragma unroll
     for (int st = 0; st < STAGES; ++st)
@@ -215,61 +211,29 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
     wait_vmcnt<(STAGES - 1) * COPIES>();
     lds_barrier();
 
-    v4i fa[MA], fb[4];
-    int sa[MA], sb[4];
+    v4i fa[NA], fb[2];
+    int sa[NA], sb[2];
 #pragma unroll
-    for (int a = 0; a < MA; ++a) {
-        fa[a] = *reinterpret_cast<const v4i*>(lds + a_lane + c0 + 2048 * a);
-        sa[a] = lds[sa_byte + 128 * a];
+    for (int a = 0; a < NA; ++a) {
+        fa[a] = *reinterpret_cast<const v4i*>(lds + a_base + 1024 * a);
+        sa[a] = lds[sa_base + 64 * a];
     }
-#pragma unroll
-    for (int b = 0; b < 4; ++b) {
-        fb[b] = *reinterpret_cast<const v4i*>(lds + b_lane + c0 + 2048 * b);
-        sb[b] = lds[sb_byte + 128 * b];
-    }
+    fb[0] = *reinterpret_cast<const v4i*>(lds + b_base);
+    sb[0] = lds[sb_base];
     __builtin_amdgcn_s_waitcnt(0xC07F);
     __builtin_amdgcn_sched_barrier(0);
 
-    constexpr int SA_[12] = {0, 0, 0, 0, 1, 2, 1, 2, 1, 2, 1, 2};
-    constexpr int SB_[12] = {0, 1, 2, 3, 0, 0, 1, 1, 2, 2, 3, 3};
-    auto mfma = [&](int i, int s) {
-        const int a = SA_[i], b = SB_[i];
-        const v8i av = {fa[a].x, fa[a].y, fa[a].z, fa[a].w, 0, 0, 0, 0};
-        const v8i bv = {fb[b].x, fb[b].y, fb[b].z, fb[b].w, 0, 0, 0, 0};
-        (void)s;
-        acc[a][b] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, acc[a][b], 4, 4, 0, sa[a], 0, sb[b]);
-    };
-    // refill after slot i with the fragments of k-step s of stage st (and, for
-    // k-step 0 of the next stage, the scale words)
-    auto refill = [&](int i, const uint8_t* st, int s) {
-        const int c = s == 0 ? c0 : c1;
-        auto fa_ = [&](int a) {
-            fa[a] = *reinterpret_cast<const v4i*>(st + a_lane + c + 2048 * a);
-            sa[a] = st[sa_byte + 128 * a + 2 * s];
-        };
-        auto fb_ = [&](int b) {
-            fb[b] = *reinterpret_cast<const v4i*>(st + b_lane + c + 2048 * b);
-            sb[b] = st[sb_byte + 128 * b + 2 * s];
-        };
-        if (i == 3) fa_(0);
-        if (i == 5) fb_(0);
-        if (i == 7) fb_(1);
-        if (i == 9) fb_(2);
-        if (i == 11) {
-            fb_(3);
-            fa_(1);
-            fa_(2);
-        }
-    };
-    // copies 0-3 of a refill go out after slots CS[] of the k-step that
-    // follows the barrier, copies 4 and 5 after slots 0 and 6 of the next
-    // stage's first k-step (before the first refill: stage STAGES - 1
-    // again, the same bytes into its slot)
+    // A stage is NB phases of NA MFMAs: phase j multiplies every A block with
+    // B block j (in fb[j & 1]), and B block j + 1 is read at the start of
+    // phase j.  The stage barrier follows MFMA BARRIER_AT (in phase NB - 2);
+    // phase NB - 1 then reads the next slot: its first B block at the phase's
+    // start and each A block right after that block's last MFMA.  Copies
+    // 0..COPIES_NOW - 1 of a refill go out after MFMAs CS[] of the stage,
+    // after the barrier, the others after MFMAs 0 and 12 of the next stage.
+    constexpr int BARRIER_AT = NA * (NB - 2) + 3;
     constexpr int COPIES_NOW = 4;
-    constexpr int CS[COPIES_NOW] = {4, 6, 8, 10};
-    constexpr int BARRIER_AFTER = 3;
-    // One stage with its ring slot known at compile time (every LDS offset an
-    // immediate); the stage loop runs in rounds of STAGES.
+    constexpr int CS[COPIES_NOW] = {BARRIER_AT + 1, BARRIER_AT + 3, BARRIER_AT + 5, BARRIER_AT + 7};
+    static_assert(BARRIER_AT + 7 < NA * NB, "copies inside the stage");
     auto stage = [&](auto slot_c, int kt) {
         constexpr int slot = decltype(slot_c)::value;
         constexpr int next = slot + 1 == STAGES ? 0 : slot + 1;
@@ -280,34 +244,38 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
         const uint8_t* cur = lds + slot * STAGE_BYTES;
         const uint8_t* nxt = lds + next * STAGE_BYTES;
 #pragma unroll
-        for (int i = 0; i < 12; ++i) {
-            __builtin_amdgcn_sched_barrier(0);
-            mfma(i, 0);
-            refill(i, cur, 1);
-            if (i == 0) issue(COPIES_NOW, prev_kt, prev_oob, prev_slot);
-            if (i == 6) issue(COPIES_NOW + 1, prev_kt, prev_oob, prev_slot);
-        }
+        for (int j = 0; j < NB; ++j) {
 #pragma unroll
-        for (int i = 0; i <= BARRIER_AFTER; ++i) {
-            __builtin_amdgcn_sched_barrier(0);
-            mfma(i, 1);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        wait_vmcnt<(STAGES - 2) * COPIES>();
-        lds_barrier();
+            for (int i = 0; i < NA; ++i) {
+                const int idx = NA * j + i;
+                __builtin_amdgcn_sched_barrier(0);
+                const v8i av = {fa[i].x, fa[i].y, fa[i].z, fa[i].w, 0, 0, 0, 0};
+                const v8i bv = {fb[j & 1].x, fb[j & 1].y, fb[j & 1].z, fb[j & 1].w, 0, 0, 0, 0};
+                acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc[i][j], 4, 4, 0, sa[i], 0,
+                                                                             sb[j & 1]);
+                if (i == 0 && j + 1 < NB) {
+                    fb[(j + 1) & 1] = *reinterpret_cast<const v4i*>(cur + b_base + 1024 * (j + 1));
+                    sb[(j + 1) & 1] = cur[sb_base + 64 * (j + 1)];
+                }
+                if (idx == 0) issue(COPIES_NOW, prev_kt, prev_oob, prev_slot);
+                if (idx == 12) issue(COPIES_NOW + 1, prev_kt, prev_oob, prev_slot);
+                if (idx == BARRIER_AT) {
+                    __builtin_amdgcn_sched_barrier(0);
+                    wait_vmcnt<(STAGES - 2) * COPIES>();
+                    lds_barrier();
+                }
+                if (j == NB - 1) {
+                    if (i == 0) {
+                        fb[0] = *reinterpret_cast<const v4i*>(nxt + b_base);
+                        sb[0] = nxt[sb_base];
+                    }
+                    fa[i] = *reinterpret_cast<const v4i*>(nxt + a_base + 1024 * i);
+                    sa[i] = nxt[sa_base + 64 * i];
+                }
 #pragma unroll
-        for (int i = 0; i < 12; ++i) {
-            __builtin_amdgcn_sched_barrier(0);
-            if (i > BARRIER_AFTER) mfma(i, 1);
-            if (i == BARRIER_AFTER) {
-#pragma unroll
-                for (int j = 0; j <= BARRIER_AFTER; ++j) refill(j, nxt, 0);
-            } else if (i > BARRIER_AFTER) {
-                refill(i, nxt, 0);
+                for (int c = 0; c < COPIES_NOW; ++c)
+                    if (CS[c] == idx) issue(c, kt + STAGES, oob, slot);
             }
-#pragma unroll
-            for (int j = 0; j < COPIES_NOW; ++j)
-                if (CS[j] == i) issue(j, kt + STAGES, oob, slot);
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -326,36 +294,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
     wait_vmcnt<0>();
 
     // Epilogue.  Lane l, register r of accumulator block (a, b) holds row
-    // 32 a + 8 (r / 4) + 4 (l / 32) + r % 4 and column 32 b + l % 32 of the
-    // wave's 96 x 128 sub-tile.  Each lane rounds its values to bf16 where
-    // they lie and parks them in its wave's part of the (now free) ring, 32
-    // rows at a time, rows padded to P16 bf16 so that the two lane halves
-    // (rows r and r + 4) write disjoint banks; the rows are then read back
-    // contiguous, 16 bytes per lane, and leave as one 16-byte store.
+    // 16 a + 4 (l / 16) + r and column 16 b + l % 16 of the wave's 96 x 128
+    // sub-tile.  Each lane rounds its values to bf16 where they lie and parks
+    // them in its wave's part of the (now free) ring, 16 rows at a time, rows
+    // padded to P16 bf16 so that the four lane quarters (rows 4 apart) write
+    // disjoint banks; the rows are then read back contiguous, 16 bytes per
+    // lane, and leave as one 16-byte store.
     lds_barrier();
-    uint16_t* st16 = reinterpret_cast<uint16_t*>(lds + wave * (32 * P16 * 2));
+    uint16_t* st16 = reinterpret_cast<uint16_t*>(lds + wave * (16 * P16 * 2));
     const int grow0 = m0 + 32 * MA * wm;
     const int cg = lane % 16, ro = lane / 16;
     const int col0 = n0 + 128 * wn + 8 * cg;
     const bool vec_cols = (col0 + 8 <= N) && (N % 8 == 0);
-    const int l31 = lane & 31, hl = lane >> 5;
+    const int q4 = lane >> 4;
 #pragma unroll
-    for (int a = 0; a < MA; ++a) {
+    for (int a = 0; a < NA; ++a) {
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int b = 0; b < 4; ++b)
+        for (int b = 0; b < NB; ++b)
 #pragma unroll
-            for (int r = 0; r < 16; r += 2) {
+            for (int r = 0; r < 4; r += 2) {
                 const uint32_t pk = pack_bf16(acc[a][b][r], acc[a][b][r + 1]);
-                const int row = 8 * (r >> 2) + 4 * hl + (r & 3);   // rows row, row + 1
-                st16[row * P16 + 32 * b + l31] = (uint16_t)pk;
-                st16[(row + 1) * P16 + 32 * b + l31] = (uint16_t)(pk >> 16);
+                const int row = 4 * q4 + r;   // rows row, row + 1
+                st16[row * P16 + 16 * b + fr] = (uint16_t)pk;
+                st16[(row + 1) * P16 + 16 * b + fr] = (uint16_t)(pk >> 16);
             }
         asm volatile("" ::: "memory");
 #pragma unroll
-        for (int it = 0; it < 8; ++it) {
+        for (int it = 0; it < 4; ++it) {
             const int lr = 4 * it + ro;
-            const int grow = grow0 + 32 * a + lr;
+            const int grow = grow0 + 16 * a + lr;
             const v4u pk = *reinterpret_cast<const v4u*>(st16 + lr * P16 + 8 * cg);
             if (grow >= M) continue;
             if (vec_cols) {
