@@ -169,8 +169,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
     // Row rr of a copy is read at rr * KB + its swizzled chunk; rows past the
     // tile's last row lie past the buffer's range and read as zeros (their
     // outputs are masked at the store).  Consecutive copies of a wave are 16
-    // rows apart and share the swizzle ((rr >> 2) & 3 = (lane >> 4) & 3).
-    const uint32_t chunk = 16u * (uint32_t)((lane & 3) ^ ((lane >> 4) & 3));
+    // rows apart and share the swizzle ((rr >> 1) & 3 = (lane >> 3) & 3).
+    const uint32_t chunk = 16u * (uint32_t)((lane & 3) ^ ((lane >> 3) & 3));
     const uint32_t voff_a = (uint32_t)(16 * MA * wave + (lane >> 2)) * (uint32_t)KB + chunk;
     const uint32_t voff_b = (uint32_t)(32 * wave + (lane >> 2)) * (uint32_t)KB + chunk;
     const uint32_t lds_base = __builtin_amdgcn_readfirstlane(
@@ -195,10 +195,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
     // takes, in lane l, row l % 16 of a 16-row block and the 32 elements (16
     // bytes) of block l / 16 of the stage's 128, with that block's scale.
     // Every block starts at a row that is a multiple of 16, so the swizzle
-    // (row >> 2) & 3 depends on the lane alone and block i of a panel lies
+    // (row >> 1) & 3 depends on the lane alone and block i of a panel lies
     // 1 KiB (codes) or 64 bytes (scale words) after block i - 1.
     const int fr = lane & 15;
-    const int fpos = 16 * ((lane >> 4) ^ ((fr >> 2) & 3));
+    const int fpos = 16 * ((lane >> 4) ^ ((fr >> 1) & 3));
     const int a_base = (32 * MA * wm + fr) * BK + fpos;
     const int b_base = A_STAGE + (128 * wn + fr) * BK + fpos;
     const int sa_base = A_STAGE + B_STAGE + 4 * (32 * MA * wm + fr) + (lane >> 4);
