@@ -242,25 +242,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     const int m0 = tile.tm * BM;
     const int rows_a = (M - m0) < BM ? (M - m0) : BM;
 
-    // Epilogue scales: s_x of the tile's row tid into a register before the
-    // main loop (parked in LDS after it, where the ring was); s_w of the
-    // lane's 8 output columns is loaded after the loop (fewer registers live
-    // across it).
+    // Epilogue scales are loaded after the main loop (no register of theirs
+    // lives across it): s_x of the tile's row tid, parked in LDS where the ring
+    // was, and s_w of the lane's output columns.
     constexpr int EPI_CG = EP == Epilogue::SWIGLU ? 8 : 16;   // column groups per wave row
     const int epi_cg = lane % EPI_CG;
     const int epi_ro = lane / EPI_CG;
     const int epi_col0 = EP == Epilogue::SWIGLU ? tile.tn * (BN / 2) + 64 * wn + 8 * epi_cg
                                                 : tile.tn * BN + 128 * wn + 8 * epi_cg;
-    float sx_own = 0.0f;
-    if constexpr (EP != Epilogue::S32) {
-        if (tid < BM) sx_own = sx[tid < rows_a ? m0 + tid : M - 1];
-    }
 
     // Copy sources.  Copy i < A_COPIES of wave w fills A slab rows
     // 16 (A_COPIES w + i) .. +15 of a stage; copy A_COPIES + i (i = 0, 1)
     // fills B slab rows 32 w + 16 i ..
     // +15.  Lane l writes row (l / 4) of its 16 at chunk position l % 4,
-    // which holds logical chunk (l % 4) ^ swz(row).  Offsets are relative to a
+    // which holds logical chunk (l % 4) ^ ((row >> 1) & 3).  Offsets are relative to a
     // per-panel buffer resource (the tile's A rows; its gate rows; its up
     // rows), whose range ends at the panel's last row.
     int b_first;   // first weight row of this tile (gate rows for SwiGLU)
@@ -422,7 +417,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     // themselves.
     const int q4 = lane >> 4;
     float swv[NB];
+    float sx_own = 0.0f;
     if constexpr (EP != Epilogue::S32) {
+        if (tid < BM) sx_own = sx[tid < rows_a ? m0 + tid : M - 1];
 #pragma unroll
         for (int b = 0; b < NB; ++b) {
             int c;
