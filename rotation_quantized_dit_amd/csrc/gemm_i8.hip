@@ -253,11 +253,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
 
     // Copy sources.  Copy i < A_COPIES of wave w fills A slab rows
     // 16 (A_COPIES w + i) .. +15 of a stage; copy A_COPIES + i (i = 0, 1)
-    // fills B slab rows 32 w + 16 i ..
-    // +15.  Lane l writes row (l / 4) of its 16 at chunk position l % 4,
-    // which holds logical chunk (l % 4) ^ ((row >> 1) & 3).  Offsets are relative to a
-    // per-panel buffer resource (the tile's A rows; its gate rows; its up
-    // rows), whose range ends at the panel's last row.
+    // fills B slab rows 32 w + 16 i .. +15.  Lane l writes row (l / 4) of its
+    // 16 at chunk position l % 4, which holds logical chunk
+    // (l % 4) ^ ((row >> 1) & 3).  Offsets are relative to a per-panel buffer
+    // resource (the tile's A rows; its gate rows; its up rows), whose range
+    // ends at the panel's last row.
     int b_first;   // first weight row of this tile (gate rows for SwiGLU)
     if constexpr (EP == Epilogue::SWIGLU)
         b_first = tile.tn * (BN / 2);
