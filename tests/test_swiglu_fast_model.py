@@ -5,9 +5,9 @@ The kernel computes, on the transcendental unit,
     h = ((g * rcp(d)) 2^-64) * u
 and keeps that h only where its low 16 bits lie more than a fixed margin of
 fp32 steps from the bf16 rounding midpoint; everywhere else it evaluates the
-definition g / (1 + exp(-g)) * u (SiLU as used by the SwiGLU feed-forward of
-the transformer blocks in "ConvRot: Rotation-Based Plug-and-Play 4-bit
-Quantization for Diffusion Transformers", section on the W4A4 linear layers).
+definition g / (1 + exp(-g)) * u with the fixed fp32 exponential (the SwiGLU
+of the FFN, h3-rs README, "Speed"; placed on fc1's output side as in the
+hybrid model card's "FFN output + SwiGLU" projection).
 
 This test models the fast evaluation in numpy over every finite bf16 gate,
 with exp2 and rcp pushed 2 ulps off their exact values in either direction,
