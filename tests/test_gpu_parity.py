@@ -83,9 +83,11 @@ def test_tiny_swiglu(cr):
 
 
 @pytest.mark.parametrize("m,n,k", [(1, 1, 256), (37, 100, 256), (300, 300, 768), (257, 513, 512),
-                                   (511, 130, 1024), (64, 256, 5376)])
+                                   (511, 130, 1024), (64, 256, 5376), (385, 257, 1280), (769, 1025, 256)])
 def test_ragged_shapes(cr, m, n, k):
-    """Ragged token and output counts: tails of partial 256-row tiles."""
+    """Ragged token and output counts: tails of partial 384 x 256 tiles and of
+    the 16-row / 16-column MFMA blocks inside them, one row or column past a
+    tile boundary, and stage counts of one and five rounds of the ring."""
     rng = np.random.default_rng(m * 7 + n * 3 + k)
     x = rng.standard_normal((m, k), dtype=np.float32)
     x[:, rng.choice(k, 3, replace=False)] *= 40
@@ -94,7 +96,7 @@ def test_ragged_shapes(cr, m, n, k):
     check_all(g, o, "ragged %dx%dx%d" % (m, n, k))
 
 
-@pytest.mark.parametrize("m,i,k", [(5, 1, 256), (300, 100, 512), (130, 200, 768)])
+@pytest.mark.parametrize("m,i,k", [(5, 1, 256), (300, 100, 512), (130, 200, 768), (385, 129, 1280)])
 def test_ragged_swiglu(cr, m, i, k):
     rng = np.random.default_rng(m + i + k)
     x = rng.laplace(size=(m, k)).astype(np.float32)
