@@ -35,8 +35,9 @@
 
 // Operand streaming.  Both operands are K-contiguous rows (q_x is [M, K] and
 // q_w is [N, K]), which is the MFMA operand layout: a lane takes 16
-// contiguous bytes of one row (row l % 16 of a 16-row block, chunk l / 16).  K advances 64 bytes per stage through a ring
-// of 4 LDS slots (40 KiB each, the whole 160 KiB).  Global -> LDS copies are
+// contiguous bytes of one row (row l % 16 of a 16-row block, chunk l / 16).
+// K advances 64 bytes per stage through a ring of 3 LDS slots (40 KiB each;
+// a fourth slot measured 0.6-0.7 % slower).  Global -> LDS copies are
 // direct buffer loads (buffer_load_dwordx4 ... lds: 64 lanes x 16 B land
 // contiguously in LDS, no VGPR staging): each wave copies 48 rows of A and 32
 // rows of B per stage, five copies.  Each LDS row is 64 bytes (4 chunks of
@@ -57,8 +58,7 @@
 // it is set.
 //
 // Main loop (one stage = 48 MFMAs per wave, 64 bytes of K), unrolled over the
-// four slots of the ring (K is a multiple of 256, so the stage count is a
-// multiple of four):
+// three slots of the ring, with a peeled remainder of one or two stages:
 //   - the stage runs as 8 phases, one per B block j: every A block times B
 //     block j.  The six A fragments stay in registers for the stage and B is
 //     double-buffered, B block j + 1 read at the start of phase j (224
@@ -69,7 +69,7 @@
 //     reads of the current slot complete;
 //   - phase 7 then reads the next slot: its first B block at the phase's
 //     start and each A block right after that block's last MFMA;
-//   - after the barrier the current slot is refilled with the stage four
+//   - after the barrier the current slot is refilled with the stage three
 //     ahead: three copies spread over the rest of the stage, the last two
 //     in the next stage's first phases.
 // Past the last stage the copies are still issued (so every stage has the
@@ -108,7 +108,7 @@ constexpr int NTHREADS = 64 * NWAVES;
 constexpr int A_STAGE = BM * BK;
 constexpr int B_STAGE = BN * BK;
 constexpr int STAGE_BYTES = A_STAGE + B_STAGE;
-constexpr int STAGES = 4;
+constexpr int STAGES = 3;
 constexpr int RING_BYTES = STAGES * STAGE_BYTES;
 // copies per wave per stage: A_COPIES of A (16 rows each) and 2 of B
 constexpr int COPIES = A_COPIES + 2;
@@ -344,10 +344,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
     constexpr int CS[COPIES_NOW] = {BARRIER_AT + 2, BARRIER_AT + 4, BARRIER_AT + 6};
     static_assert(BARRIER_AT + 6 < NA * NB, "copies inside the stage");
 
-    // One stage with its ring slot known at compile time; K is a multiple of
-    // 256, so the stage count is a multiple of STAGES and the loop runs whole
-    // rounds.
-    static_assert(256 % (STAGES * BK) == 0, "whole rounds of STAGES stages");
+    // One stage with its ring slot known at compile time (every slot offset a
+    // constant); the loop runs in rounds of STAGES, then the remainder.
     auto stage = [&](auto slot_c, int kt) {
         constexpr int slot = decltype(slot_c)::value;
         constexpr int next = slot + 1 == STAGES ? 0 : slot + 1;
@@ -391,14 +389,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
         }
         __builtin_amdgcn_sched_barrier(0);
     };
-    static_assert(STAGES == 4, "rounds of four stages");
-    for (int kt = 0; kt < KT; kt += 4) {
+    static_assert(STAGES == 3, "rounds of three stages");
+    int kt = 0;
+    for (; kt + 3 <= KT; kt += 3) {
         stage(std::integral_constant<int, 0>{}, kt);
         stage(std::integral_constant<int, 1>{}, kt + 1);
         stage(std::integral_constant<int, 2>{}, kt + 2);
-        stage(std::integral_constant<int, 3>{}, kt + 3);
     }
-    const int prev_slot = STAGES - 1;
+    if (kt < KT) stage(std::integral_constant<int, 0>{}, kt);
+    if (kt + 1 < KT) stage(std::integral_constant<int, 1>{}, kt + 1);
+    const int prev_slot = (KT - 1) % STAGES;
     const uint32_t prev_soff = (uint32_t)(KT - 1 + STAGES) * BK;
     // the deferred copies of the last refill (out of range), then no copy may
     // still be writing the ring, which the epilogue reuses
