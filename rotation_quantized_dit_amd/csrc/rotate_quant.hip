@@ -94,11 +94,14 @@ struct F32Rows {    // weights, fp32 [rows, k]
     struct Raw {
         v4f t[4];
     };
+    // Ordinary loads here: for fp32 rows they stream about 1.4x faster than
+    // the nontemporal form the bf16 sources use (same kernel, 28672 x 5376
+    // and 5376 x 14336 weights on MI355X: 5.4-5.5 against 3.9-4.0 TB/s).
     __device__ __forceinline__ Raw fetch(int64_t row, int64_t k, int64_t off) const {
         const v4f* q = reinterpret_cast<const v4f*>(x + row * k + off);
         Raw r;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) r.t[i] = __builtin_nontemporal_load(q + i);
+        for (int i = 0; i < 4; ++i) r.t[i] = q[i];
         return r;
     }
     __device__ __forceinline__ void expand(const Raw& r, float v[16]) const {
