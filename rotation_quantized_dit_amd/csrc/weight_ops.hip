@@ -83,6 +83,12 @@ __global__ __launch_bounds__(256) void lora_add_kernel(float* __restrict__ w, in
     const int64_t c0 = ((int64_t)(blockIdx.x % col_blocks) * 256 + threadIdx.x) * 4;
     const int64_t r0 = (int64_t)(blockIdx.x / col_blocks) * kRows;
     if (c0 >= k) return;   // k % 256 == 0, so c0 < k covers all four columns
+    // The rows of W this thread updates are loaded first, so that their
+    // memory latency overlaps the rank loop.
+    v4f x[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r)
+        if (r0 + r < n) x[r] = *reinterpret_cast<const v4f*>(w + (r0 + r) * k + c0);
     float acc[kRows][4];
 #pragma unroll
     for (int r = 0; r < kRows; ++r)
@@ -104,13 +110,12 @@ __global__ __launch_bounds__(256) void lora_add_kernel(float* __restrict__ w, in
     for (int r = 0; r < kRows; ++r) {
         const int64_t row = r0 + r;
         if (row >= n) break;
-        v4f* p = reinterpret_cast<v4f*>(w + row * k + c0);
-        v4f x = *p;
-        x.x = x.x + scale * acc[r][0];
-        x.y = x.y + scale * acc[r][1];
-        x.z = x.z + scale * acc[r][2];
-        x.w = x.w + scale * acc[r][3];
-        *p = x;
+        v4f y = x[r];
+        y.x = y.x + scale * acc[r][0];
+        y.y = y.y + scale * acc[r][1];
+        y.z = y.z + scale * acc[r][2];
+        y.w = y.w + scale * acc[r][3];
+        *reinterpret_cast<v4f*>(w + row * k + c0) = y;
     }
 }
 
