@@ -224,8 +224,11 @@ def qkv_bench(torch, cr, dev, steps):
     ws = torch.empty(cr.workspace_bytes(M, K), dtype=torch.uint8, device=dev)
     n = max(5, min(steps, 20))
 
+    # 50 untimed launches first (10-20 ms of GPU work, like the FFN step's
+    # warmup): with only 3, the GEMM's median read about 20 % above its
+    # steady-state time, measured right after the host-side input generation
     def time_it(fn):
-        for _ in range(3):
+        for _ in range(50):
             fn()
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(n + 1)]
         ev[0].record()
